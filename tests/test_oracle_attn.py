@@ -1,0 +1,226 @@
+"""Pins for the oracle's verification and prefill attention.
+
+The attention the method computes is ordinary masked softmax attention; packing and tile
+routing only reorganise it (DScale Sec. III-B/III-D).  The oracle is pinned to:
+  * the three formulations agreeing exactly (packed / one request at a time / padded with a
+    materialised mask),
+  * softmax rows summing to one,
+  * closed forms (constant V, all-zero K, one dominant key),
+  * torch's fp64 CPU scaled_dot_product_attention on the special cases that reduce to it
+    (single-query decode, textbook causal prefill), with an explicit boolean mask,
+  * brute force on the tiny fp32 workload (materialised mask and probabilities).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+
+
+def _small_case(seed=11, dtype="bf16", hq=4, hkv=2, d=32, k=(3, 16, 1, 0, 7), ctx=(5, 40, 0, 9, 70),
+                extra_tail=3):
+    k = np.asarray(k, np.int32)
+    return wl.make_case(seed, dtype=dtype, hq=hq, hkv=hkv, d=d, k=k, ctx_len=ctx,
+                        m_bs=int(k.sum()) + extra_tail, qkv_scale=0.7)
+
+
+def _offsets(c):
+    return oracle.pack(c["k"], c["ctx_len"], c["kv_base"], c["block_tokens"], c["W"], c["m_bs"])["offsets"]
+
+
+def _f64(a):
+    if a.dtype == np.uint16:
+        return wl.bf16_bits_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def _run3(c, use_new=True):
+    off = _offsets(c)
+    kn = c["k_new"] if use_new else None
+    vn = c["v_new"] if use_new else None
+    args = (c["q"], c["k_pool"], c["v_pool"], off, c["k"], c["ctx_len"], c["kv_base"])
+    p = oracle.verify_attn(*args, k_new=kn, v_new=vn)
+    r = oracle.attn_per_request(*args, k_new=kn, v_new=vn)
+    pad = oracle.attn_padded(*args, c["W"], k_new=kn, v_new=vn)
+    return off, p, r, pad
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("use_new", [True, False])
+def test_three_formulations_agree(dtype, use_new):
+    c = _small_case(dtype=dtype)
+    off, (po, pl), (ro, rl), (ao, al) = _run3(c, use_new)
+    end = int(off[-1])
+    assert np.array_equal(po[:end], ro[:end]) and np.array_equal(pl[:end], rl[:end])
+    assert np.array_equal(po[:end], ao[:end]) and np.array_equal(pl[:end], al[:end])
+    assert np.all(po[end:] == 0) and np.all(np.isneginf(pl[end:]))
+    assert np.all(np.isfinite(po[:end]))
+
+
+def test_softmax_rows_sum_to_one():
+    r = np.random.default_rng(5)
+    for n in (1, 2, 17, 300):
+        q = wl.to_bf16_bits(r.standard_normal(64).astype(np.float32) * 3)
+        K = wl.to_bf16_bits(r.standard_normal((n, 64)).astype(np.float32))
+        p = oracle.softmax_probs(q, K)
+        assert abs(p.sum() - 1.0) <= 1e-12 and np.all(p >= 0)
+
+
+def _sequence(c, i, off):
+    """Request i's key/value sequence in position order (context rows, then k_new)."""
+    b, cx, kk = int(c["kv_base"][i]), int(c["ctx_len"][i]), int(c["k"][i])
+    K = _f64(c["k_pool"][:, b:b + cx + kk]).copy()
+    V = _f64(c["v_pool"][:, b:b + cx + kk]).copy()
+    K[:, cx:cx + kk] = np.transpose(_f64(c["k_new"][off[i]:off[i] + kk]), (1, 0, 2))
+    V[:, cx:cx + kk] = np.transpose(_f64(c["v_new"][off[i]:off[i] + kk]), (1, 0, 2))
+    return K, V
+
+
+def test_closed_forms():
+    c = _small_case(seed=12, dtype="f32", hq=2, hkv=1, d=16, k=(4, 2), ctx=(10, 3))
+    off = _offsets(c)
+    # constant V -> output equals that constant row
+    const = np.linspace(-2, 2, 16).astype(np.float32)
+    c1 = dict(c, v_pool=np.broadcast_to(const, c["v_pool"].shape).copy(),
+              v_new=np.broadcast_to(const, c["v_new"].shape).copy())
+    o, _ = oracle.verify_attn(c1["q"], c1["k_pool"], c1["v_pool"], off, c1["k"], c1["ctx_len"],
+                              c1["kv_base"], c1["k_new"], c1["v_new"])
+    assert np.allclose(o[: off[-1]], const, atol=1e-12)
+    # all-zero K -> uniform weights: output is the mean of the visible V rows, lse = ln(n)
+    c2 = dict(c, k_pool=np.zeros_like(c["k_pool"]), k_new=np.zeros_like(c["k_new"]))
+    o, l = oracle.verify_attn(c2["q"], c2["k_pool"], c2["v_pool"], off, c2["k"], c2["ctx_len"],
+                              c2["kv_base"], c2["k_new"], c2["v_new"])
+    for i in range(c["n_bs"]):
+        _, V = _sequence(c2, i, off)
+        for j in range(int(c["k"][i])):
+            n = int(c["ctx_len"][i]) + j + 1
+            s = off[i] + j
+            assert np.allclose(o[s, 0], V[0, :n].mean(axis=0), atol=1e-12)
+            assert abs(l[s, 0] - np.log(n)) < 1e-12
+    # one dominant key -> output is (almost exactly) that key's V row
+    c3 = dict(c, k_pool=np.zeros_like(c["k_pool"]), k_new=np.zeros_like(c["k_new"]))
+    q = np.zeros_like(c["q"])
+    q[:, :, 0] = 1.0
+    kp = c3["k_pool"].copy()
+    b = int(c["kv_base"][0])
+    kp[0, b + 5, 0] = 60.0  # position 5 of request 0 dominates by e^15
+    o, _ = oracle.verify_attn(q, kp, c3["v_pool"], off, c3["k"], c3["ctx_len"], c3["kv_base"],
+                              c3["k_new"], c3["v_new"])
+    assert np.allclose(o[0, 0], c3["v_pool"][0, b + 5], atol=1e-4)
+
+
+def _sdpa(qrows, K, V, mask, scale):
+    """torch fp64 CPU SDPA with an explicit boolean mask: qrows [n_q, d], K/V [n_k, d]."""
+    q = torch.from_numpy(qrows)[None, None]
+    k = torch.from_numpy(K)[None, None]
+    v = torch.from_numpy(V)[None, None]
+    m = torch.from_numpy(mask)[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=m, scale=scale)[0, 0].numpy()
+
+
+def test_single_query_decode_matches_sdpa():
+    """k_i = 1 (anchor only) is plain single-query decode attention over ctx + 1 keys."""
+    c = _small_case(seed=13, dtype="bf16", hq=4, hkv=2, d=32, k=(1, 1, 1), ctx=(0, 31, 200), extra_tail=0)
+    off = _offsets(c)
+    o, l = oracle.verify_attn(c["q"], c["k_pool"], c["v_pool"], off, c["k"], c["ctx_len"],
+                              c["kv_base"], c["k_new"], c["v_new"])
+    q64 = _f64(c["q"])
+    for i in range(3):
+        K, V = _sequence(c, i, off)
+        for h in range(4):
+            g = h // 2
+            n = K.shape[1]
+            ref = _sdpa(q64[off[i], h][None], K[g], V[g], np.ones((1, n), bool), 1 / np.sqrt(32))
+            assert np.allclose(o[off[i], h], ref[0], rtol=1e-12, atol=1e-12)
+            z = (K[g] @ q64[off[i], h]) / np.sqrt(32)
+            assert abs(l[off[i], h] - torch.logsumexp(torch.from_numpy(z), 0).item()) < 1e-12
+
+
+def test_verify_block_matches_sdpa_with_mask():
+    """A full 16-slot block over a context: rows see the whole context and a causal prefix of
+    the block (DScale Sec. III-D request-local causal mask)."""
+    c = _small_case(seed=14, dtype="f32", hq=6, hkv=2, d=16, k=(16, 5), ctx=(23, 0), extra_tail=2)
+    off = _offsets(c)
+    o, _ = oracle.verify_attn(c["q"], c["k_pool"], c["v_pool"], off, c["k"], c["ctx_len"],
+                              c["kv_base"], c["k_new"], c["v_new"])
+    q64 = _f64(c["q"])
+    for i in range(2):
+        K, V = _sequence(c, i, off)
+        kk, cx = int(c["k"][i]), int(c["ctx_len"][i])
+        mask = np.zeros((kk, cx + kk), bool)
+        for j in range(kk):
+            mask[j, : cx + j + 1] = True
+        for h in range(6):
+            ref = _sdpa(q64[off[i]:off[i] + kk, h], K[h // 3], V[h // 3], mask, 0.25)
+            assert np.allclose(o[off[i]:off[i] + kk, h], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_prefill_matches_textbook_causal():
+    """Fresh prefill (context 0) is textbook causal attention (is_causal=True in SDPA)."""
+    r = wl.rng(99, 0)
+    hq, hkv, d, L = 4, 1, 32, 70
+    pool_k = wl.normal(r, (hkv, 200, d), 0.8, "bf16")
+    pool_v = wl.normal(r, (hkv, 200, d), 0.8, "bf16")
+    q = wl.normal(r, (L + 30, hq, d), 0.8, "bf16")
+    # request 0: rows 0..L-1 at pool rows 100.., request 1: 30 rows after a 12-row context
+    q_start, q_len, ctx, base = [0, L], [L, 30], [0, 12], [100, 40]
+    sel_req = [0] * L + [1] * 30
+    sel_j = list(range(L)) + list(range(30))
+    o, l = oracle.prefill_attn(q, pool_k, pool_v, q_start, q_len, ctx, base, sel_req, sel_j)
+    qq = torch.from_numpy(_f64(q[:L]).transpose(1, 0, 2))[None]
+    kk = torch.from_numpy(_f64(pool_k[:, 100:100 + L]))[None].expand(1, hq, L, d)
+    vv = torch.from_numpy(_f64(pool_v[:, 100:100 + L]))[None].expand(1, hq, L, d)
+    ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, is_causal=True)[0].numpy()
+    assert np.allclose(o[:L], ref.transpose(1, 0, 2), rtol=1e-12, atol=1e-12)
+    # request 1 with context: explicit mask over 12 + 30 keys
+    K = _f64(pool_k[0, 40:40 + 42])
+    V = _f64(pool_v[0, 40:40 + 42])
+    mask = np.zeros((30, 42), bool)
+    for j in range(30):
+        mask[j, : 12 + j + 1] = True
+    for h in range(hq):
+        ref = _sdpa(_f64(q[L:L + 30, h]), K, V, mask, 1 / np.sqrt(d))
+        assert np.allclose(o[L:, h], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_prefill_equals_verify_on_short_rows():
+    """A prefill request with <= W rows is the same computation as a verification request
+    whose candidates already sit in the pool (different oracle entry points)."""
+    c = _small_case(seed=15, dtype="bf16", hq=4, hkv=2, d=32, k=(6, 9), ctx=(17, 4), extra_tail=0)
+    off = _offsets(c)
+    o_v, l_v = oracle.verify_attn(c["q"], c["k_pool"], c["v_pool"], off, c["k"], c["ctx_len"], c["kv_base"])
+    sel_req = [0] * 6 + [1] * 9
+    sel_j = list(range(6)) + list(range(9))
+    o_p, l_p = oracle.prefill_attn(c["q"], c["k_pool"], c["v_pool"], off[:-1], c["k"], c["ctx_len"],
+                                   c["kv_base"], sel_req, sel_j)
+    assert np.array_equal(o_v, o_p) and np.array_equal(l_v, l_p)
+
+
+def test_config1_bruteforce():
+    """Tiny fp32 workload: brute force with a materialised mask and probabilities."""
+    c = wl.config1()
+    off = _offsets(c)
+    o, l = oracle.verify_attn(c["q"], c["k_pool"], c["v_pool"], off, c["k"], c["ctx_len"],
+                              c["kv_base"], c["k_new"], c["v_new"])
+    q64 = _f64(c["q"])
+    for i in range(2):
+        K, V = _sequence(c, i, off)
+        n_all = K.shape[1]
+        for j in range(int(c["k"][i])):
+            visible = np.arange(n_all) <= int(c["ctx_len"][i]) + j
+            for h in range(2):
+                z = np.where(visible, K[0] @ q64[off[i] + j, h] / 8.0, -np.inf)
+                p = np.exp(z - z.max())
+                p /= p.sum()
+                assert np.allclose(o[off[i] + j, h], p @ V[0], rtol=1e-12, atol=1e-13)
+                assert abs(l[off[i] + j, h] - (z.max() + np.log(np.exp(z - z.max()).sum()))) < 1e-12
+
+
+def test_errors():
+    c = _small_case(seed=16)
+    off = _offsets(c)
+    bad = c["kv_base"].copy()
+    bad[-1] = c["pool_rows"]  # segment past the pool
+    with pytest.raises(oracle.OracleError):
+        oracle.verify_attn(c["q"], c["k_pool"], c["v_pool"], off, c["k"], c["ctx_len"], bad)
