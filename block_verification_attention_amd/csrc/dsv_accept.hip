@@ -1,0 +1,322 @@
+// Greedy prefix verifier, output builder and draft top-1/top-2 margin.
+//
+// DScale (arXiv HTML), Sec. III-D "Prefix verifier": in greedy decoding a deterministic
+// top-1 draft is accepted when the target picks it; after a_i accepted candidates, row
+// offset_i + a_i supplies the successor, and the output is the accepted candidates followed
+// by that successor.  Sec. II-B / Fig. 2: progress counts one anchor plus accepted drafts.
+// Sec. II-B / Fig. 4 and DFlash-Mini-Lab (DFlash7-ACT): the gap between the top-1 and top-2
+// draft logits is the acceptance signal.
+//
+// Both vocabulary sweeps are HBM-bound streams over fp32 logits.  Each row is cut into
+// chunks so that the launch has thousands of workgroups for 256 CUs; a chunk reduces to one
+// 64-bit key per row (argmax) or one (top-1 key, top-2 value) pair (margin), and a small
+// per-request kernel merges the chunks in a fixed order, so results are deterministic.
+//
+// Argmax key: (order-preserving bits of the value) << 32 | ~index.  The largest key has the
+// largest value and, among equal values, the lowest index; -0.0 is folded onto +0.0.  A NaN
+// anywhere in a row makes the chunk report the all-ones key, which dominates the merge.
+#include "dsv_internal.h"
+
+namespace dsv {
+
+constexpr int kAccThreads = 256;
+constexpr uint64_t kNanKey = ~0ull;
+
+struct Top2 {
+  uint64_t k1;  // key of the largest element (value bits << 32 | ~index); 0 = none
+  uint32_t v2;  // ordered bits of the second element of the descending multiset; 0 = none
+  uint32_t nan;
+};
+
+__device__ __forceinline__ void top2_push(Top2 &t, float x, uint32_t idx) {
+  if (x != x) {
+    t.nan = 1;
+    return;
+  }
+  uint32_t o = ordered_bits(x);
+  uint64_t key = ((uint64_t)o << 32) | (uint32_t)~idx;
+  if (key > t.k1) {
+    uint32_t prev = (uint32_t)(t.k1 >> 32);
+    t.v2 = prev > t.v2 ? prev : t.v2;
+    t.k1 = key;
+  } else {
+    t.v2 = o > t.v2 ? o : t.v2;
+  }
+}
+
+__device__ __forceinline__ Top2 top2_merge(Top2 a, Top2 b) {
+  Top2 r;
+  r.k1 = a.k1 > b.k1 ? a.k1 : b.k1;
+  uint64_t lo = a.k1 > b.k1 ? b.k1 : a.k1;
+  uint32_t v = a.v2 > b.v2 ? a.v2 : b.v2;
+  uint32_t lo_v = (uint32_t)(lo >> 32);
+  r.v2 = lo_v > v ? lo_v : v;
+  r.nan = a.nan | b.nan;
+  return r;
+}
+
+// One workgroup per (row, chunk) of a [rows][vocab] fp32 matrix.
+template <bool kVec4>
+__global__ __launch_bounds__(kAccThreads) void argmax_partial_kernel(
+    const float *__restrict__ logits, int64_t vocab, int chunk, int n_chunks, int m_bs,
+    const int32_t *__restrict__ offsets, int n_bs, uint64_t *__restrict__ keys, int32_t *status) {
+  const int64_t bid = blockIdx.x;
+  const int row = (int)(bid / n_chunks), c = (int)(bid % n_chunks);
+  int end = offsets[n_bs];
+  end = end < 0 ? 0 : (end > m_bs ? m_bs : end);
+  if (row >= end) return;
+  const int64_t lo = (int64_t)c * chunk;
+  const int64_t hi = min(vocab, lo + chunk);
+  const float *x = logits + (int64_t)row * vocab;
+  uint64_t best = 0;
+  bool nan = false;
+  const int t = threadIdx.x;
+  if (kVec4) {
+    for (int64_t v = lo + 4 * t; v < hi; v += 4 * kAccThreads) {
+      float4 f = *reinterpret_cast<const float4 *>(x + v);
+      float e[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        nan |= e[u] != e[u];
+        uint64_t key = ((uint64_t)ordered_bits(e[u]) << 32) | (uint32_t)~(uint32_t)(v + u);
+        best = key > best ? key : best;
+      }
+    }
+  } else {
+    for (int64_t v = lo + t; v < hi; v += kAccThreads) {
+      float e = x[v];
+      nan |= e != e;
+      uint64_t key = ((uint64_t)ordered_bits(e) << 32) | (uint32_t)~(uint32_t)v;
+      best = key > best ? key : best;
+    }
+  }
+  if (nan) best = kNanKey;
+  best = wave_max_u64(best);
+  __shared__ uint64_t red[kAccThreads / kWave];
+  if ((t & (kWave - 1)) == 0) red[t / kWave] = best;
+  __syncthreads();
+  if (t == 0) {
+    uint64_t r = red[0];
+    for (int w = 1; w < kAccThreads / kWave; ++w) r = red[w] > r ? red[w] : r;
+    keys[(int64_t)row * n_chunks + c] = r;
+    if (r == kNanKey) status_or(status, DSV_STATUS_NAN);
+  }
+}
+
+template <bool kVec4>
+__global__ __launch_bounds__(kAccThreads) void top2_partial_kernel(
+    const float *__restrict__ logits, int64_t vocab, int chunk, int n_chunks,
+    Top2 *__restrict__ part, int32_t *status) {
+  const int64_t bid = blockIdx.x;
+  const int64_t row = bid / n_chunks;
+  const int c = (int)(bid % n_chunks);
+  const int64_t lo = (int64_t)c * chunk;
+  const int64_t hi = min(vocab, lo + chunk);
+  const float *x = logits + row * vocab;
+  Top2 acc{0ull, 0u, 0u};
+  const int t = threadIdx.x;
+  if (kVec4) {
+    for (int64_t v = lo + 4 * t; v < hi; v += 4 * kAccThreads) {
+      float4 f = *reinterpret_cast<const float4 *>(x + v);
+      top2_push(acc, f.x, (uint32_t)v);
+      top2_push(acc, f.y, (uint32_t)v + 1);
+      top2_push(acc, f.z, (uint32_t)v + 2);
+      top2_push(acc, f.w, (uint32_t)v + 3);
+    }
+  } else {
+    for (int64_t v = lo + t; v < hi; v += kAccThreads) top2_push(acc, x[v], (uint32_t)v);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    Top2 o;
+    o.k1 = shfl_xor_u64(acc.k1, m);
+    o.v2 = (uint32_t)__shfl_xor((int)acc.v2, m);
+    o.nan = (uint32_t)__shfl_xor((int)acc.nan, m);
+    acc = top2_merge(acc, o);
+  }
+  __shared__ Top2 red[kAccThreads / kWave];
+  if ((t & (kWave - 1)) == 0) red[t / kWave] = acc;
+  __syncthreads();
+  if (t == 0) {
+    Top2 r = red[0];
+    for (int w = 1; w < kAccThreads / kWave; ++w) r = top2_merge(r, red[w]);
+    part[row * n_chunks + c] = r;
+    if (r.nan) status_or(status, DSV_STATUS_NAN);
+  }
+}
+
+// Target choice of slot s from its chunk keys (-1 for a NaN row).
+__device__ __forceinline__ int32_t argmax_from_keys(const uint64_t *keys, int64_t s, int n_chunks) {
+  uint64_t r = 0;
+  for (int c = 0; c < n_chunks; ++c) {
+    uint64_t v = keys[s * n_chunks + c];
+    r = v > r ? v : r;
+  }
+  return r == kNanKey ? -1 : (int32_t)(~(uint32_t)r);
+}
+
+// One wavefront per request.
+__global__ __launch_bounds__(kWave) void accept_finalize_kernel(
+    int n_bs, int m_bs, int W, const int32_t *__restrict__ slot_tok,
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ k,
+    const uint64_t *__restrict__ keys, int n_chunks, int32_t *__restrict__ slot_argmax,
+    int32_t *__restrict__ accepted, int32_t *__restrict__ bonus, int32_t *__restrict__ progress,
+    int32_t *__restrict__ out_tokens, const Top2 *__restrict__ dpart, int n_pos,
+    int n_chunks_d, float *__restrict__ margin, int32_t *__restrict__ draft_top1,
+    int32_t *status) {
+  const int i = blockIdx.x;
+  const int lane = threadIdx.x;
+  if (keys) {
+    int end = offsets[n_bs];
+    end = end < 0 ? 0 : (end > m_bs ? m_bs : end);
+    // every slot's choice: grid-stride over all m_bs slots
+    for (int64_t s = (int64_t)i * kWave + lane; s < m_bs; s += (int64_t)n_bs * kWave)
+      slot_argmax[s] = s < end ? argmax_from_keys(keys, s, n_chunks) : -1;
+
+    const int ki = k[i], off = offsets[i];
+    const bool ok = ki >= 0 && ki <= W && off >= 0 && (int64_t)off + ki <= end;
+    if (!ok) {
+      if (lane == 0) {
+        status_or(status, DSV_STATUS_BAD_REQUEST);
+        accepted[i] = -1;
+        bonus[i] = -1;
+        progress[i] = 0;
+      }
+      if (out_tokens && lane < W) out_tokens[(int64_t)i * W + lane] = -1;
+    } else if (ki == 0) {
+      if (lane == 0) {
+        accepted[i] = 0;
+        bonus[i] = -1;
+        progress[i] = 0;
+      }
+      if (out_tokens && lane < W) out_tokens[(int64_t)i * W + lane] = -1;
+    } else {
+      // lane j holds the target's choice at slot off + j and the draft token there
+      const int32_t g = lane < ki ? argmax_from_keys(keys, off + lane, n_chunks) : -1;
+      const int32_t tok = lane < ki ? slot_tok[off + lane] : -1;
+      const int32_t g_prev = __shfl(g, lane > 0 ? lane - 1 : 0);
+      const bool mismatch = lane >= 1 && lane < ki && tok != g_prev;
+      const uint64_t mm = __ballot(mismatch);
+      const int a = mm ? (__ffsll((long long)mm) - 1) - 1 : ki - 1;
+      const int32_t b = __shfl(g, a);
+      if (lane == 0) {
+        accepted[i] = a;
+        bonus[i] = b;
+        progress[i] = 1 + a;
+      }
+      if (out_tokens && lane < W) {
+        const int32_t next_tok = __shfl(tok, lane + 1 < kWave ? lane + 1 : lane);
+        out_tokens[(int64_t)i * W + lane] = lane < a ? next_tok : (lane == a ? b : -1);
+      }
+    }
+  }
+  if (dpart) {
+    for (int p = lane; p < n_pos; p += kWave) {
+      const int64_t row = (int64_t)i * n_pos + p;
+      Top2 r{0ull, 0u, 0u};
+      for (int c = 0; c < n_chunks_d; ++c) r = top2_merge(r, dpart[row * n_chunks_d + c]);
+      if (r.nan) {
+        margin[row] = __uint_as_float(0x7fc00000u);
+        if (draft_top1) draft_top1[row] = -1;
+      } else {
+        margin[row] = from_ordered_bits((uint32_t)(r.k1 >> 32)) - from_ordered_bits(r.v2);
+        if (draft_top1) draft_top1[row] = (int32_t)(~(uint32_t)r.k1);
+      }
+    }
+  }
+}
+
+// Chunking of a [rows][vocab] sweep: about 2048+ workgroups, chunks of >= 2048 elements,
+// multiples of 1024 (four per lane of a 256-thread workgroup).
+static void plan_chunks(int64_t rows, int64_t vocab, int *n_chunks, int *chunk) {
+  int64_t want = rows > 0 ? (2048 + rows - 1) / rows : 1;
+  int64_t cap = (vocab + 2047) / 2048;
+  if (cap < 1) cap = 1;
+  int64_t n = want < 1 ? 1 : (want > cap ? cap : want);
+  int64_t c = (vocab + n - 1) / n;
+  c = (c + 1023) / 1024 * 1024;
+  n = (vocab + c - 1) / c;
+  *n_chunks = (int)(n < 1 ? 1 : n);
+  *chunk = (int)c;
+}
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace dsv
+
+extern "C" size_t dsv_accept_workspace_bytes(int32_t m_bs, int32_t vocab, int32_t n_bs,
+                                             int32_t n_pos, int32_t draft_vocab) {
+  size_t bytes = 0;
+  int nc, ch;
+  if (m_bs > 0 && vocab > 0) {
+    dsv::plan_chunks(m_bs, vocab, &nc, &ch);
+    bytes += dsv::align256((size_t)m_bs * nc * sizeof(uint64_t));
+  }
+  if (n_bs > 0 && n_pos > 0 && draft_vocab > 0) {
+    dsv::plan_chunks((int64_t)n_bs * n_pos, draft_vocab, &nc, &ch);
+    bytes += dsv::align256((size_t)n_bs * n_pos * nc * sizeof(dsv::Top2));
+  }
+  return bytes;
+}
+
+extern "C" dsv_status dsv_accept(int32_t n_bs, int32_t m_bs, int32_t W, int32_t vocab,
+                                 const float *target_logits, const int32_t *slot_tok,
+                                 const int32_t *offsets, const int32_t *k, int32_t *slot_argmax,
+                                 int32_t *accepted, int32_t *bonus, int32_t *progress,
+                                 int32_t *out_tokens, const float *draft_logits, int32_t n_pos,
+                                 int32_t draft_vocab, float *margin, int32_t *draft_top1,
+                                 void *workspace, size_t workspace_bytes, int32_t *status,
+                                 hipStream_t stream) {
+  using namespace dsv;
+  if (n_bs < 0 || m_bs < 0 || W < 1 || W > DSV_MAX_W || !status) return DSV_ERR_INVALID_ARG;
+  const bool tgt = target_logits != nullptr;
+  const bool drf = draft_logits != nullptr;
+  if (tgt && (vocab < 1 || !slot_tok || !offsets || !k || !slot_argmax || !accepted || !bonus ||
+              !progress))
+    return DSV_ERR_INVALID_ARG;
+  if (drf && (n_pos < 1 || draft_vocab < 2 || !margin)) return DSV_ERR_INVALID_ARG;
+  if (n_bs == 0 || (!tgt && !drf)) return DSV_OK;
+  const size_t need = dsv_accept_workspace_bytes(tgt ? m_bs : 0, tgt ? vocab : 0, drf ? n_bs : 0,
+                                                 drf ? n_pos : 0, drf ? draft_vocab : 0);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return DSV_ERR_WORKSPACE;
+
+  char *ws = static_cast<char *>(workspace);
+  uint64_t *keys = nullptr;
+  int nc_t = 1, ch_t = 0, nc_d = 1, ch_d = 0;
+  if (tgt && m_bs > 0) {
+    plan_chunks(m_bs, vocab, &nc_t, &ch_t);
+    keys = reinterpret_cast<uint64_t *>(ws);
+    ws += align256((size_t)m_bs * nc_t * sizeof(uint64_t));
+    const bool vec = (vocab % 4 == 0) && ((uintptr_t)target_logits % 16 == 0);
+    const int64_t grid = (int64_t)m_bs * nc_t;
+    if (vec)
+      hipLaunchKernelGGL(argmax_partial_kernel<true>, dim3((unsigned)grid), dim3(kAccThreads), 0,
+                         stream, target_logits, (int64_t)vocab, ch_t, nc_t, m_bs, offsets, n_bs,
+                         keys, status);
+    else
+      hipLaunchKernelGGL(argmax_partial_kernel<false>, dim3((unsigned)grid), dim3(kAccThreads), 0,
+                         stream, target_logits, (int64_t)vocab, ch_t, nc_t, m_bs, offsets, n_bs,
+                         keys, status);
+    DSV_LAUNCH_CHECK();
+  }
+  Top2 *dpart = nullptr;
+  if (drf) {
+    const int64_t rows = (int64_t)n_bs * n_pos;
+    plan_chunks(rows, draft_vocab, &nc_d, &ch_d);
+    dpart = reinterpret_cast<Top2 *>(ws);
+    const bool vec = (draft_vocab % 4 == 0) && ((uintptr_t)draft_logits % 16 == 0);
+    const int64_t grid = rows * nc_d;
+    if (vec)
+      hipLaunchKernelGGL(top2_partial_kernel<true>, dim3((unsigned)grid), dim3(kAccThreads), 0,
+                         stream, draft_logits, (int64_t)draft_vocab, ch_d, nc_d, dpart, status);
+    else
+      hipLaunchKernelGGL(top2_partial_kernel<false>, dim3((unsigned)grid), dim3(kAccThreads), 0,
+                         stream, draft_logits, (int64_t)draft_vocab, ch_d, nc_d, dpart, status);
+    DSV_LAUNCH_CHECK();
+  }
+  hipLaunchKernelGGL(accept_finalize_kernel, dim3(n_bs), dim3(kWave), 0, stream, n_bs, m_bs, W,
+                     slot_tok, offsets, k, keys, nc_t, slot_argmax, accepted, bonus, progress,
+                     out_tokens, dpart, n_pos, nc_d, margin, draft_top1, status);
+  DSV_LAUNCH_CHECK();
+  return DSV_OK;
+}

@@ -1,0 +1,82 @@
+// Internal helpers of libdsv (device code for gfx950 and host-side checks).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dsv.h"
+
+namespace dsv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// bf16 <-> f32 (storage is raw uint16 bit patterns)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (finite and infinite inputs; NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------------------
+// Order-preserving float -> uint32 map used for argmax / top-2 keys.
+// -0.0 is folded onto +0.0 so that the two compare equal.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t ordered_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float from_ordered_bits(uint32_t o) {
+  uint32_t u = (o & 0x80000000u) ? (o ^ 0x80000000u) : ~o;
+  return __uint_as_float(u);
+}
+
+// ---------------------------------------------------------------------------
+// Wavefront reductions (64 lanes)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  uint32_t lo = __shfl_xor((int)(uint32_t)v, m);
+  uint32_t hi = __shfl_xor((int)(uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    uint64_t o = shfl_xor_u64(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    uint32_t o = (uint32_t)__shfl_xor((int)v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ void status_or(int32_t *status, int32_t bits) {
+  if (status) atomicOr(status, bits);
+}
+
+}  // namespace dsv
+
+// Host-side launch check: returns DSV_ERR_HIP from the enclosing function on failure.
+#define DSV_LAUNCH_CHECK()                              \
+  do {                                                  \
+    if (hipGetLastError() != hipSuccess) return DSV_ERR_HIP; \
+  } while (0)

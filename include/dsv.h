@@ -1,0 +1,250 @@
+/*
+ * dsv.h -- C ABI of libdsv: packed block verification for block-diffusion
+ * speculative decoding on AMD Instinct MI355X (gfx950).
+ *
+ * The library implements the target-side verification step described in
+ * "DScale: Scaling Block-Diffusion Speculative Decoding with Adaptive
+ * Verification" (arXiv HTML): each request brings one known anchor token
+ * followed by draft candidates (Sec. II-A/II-B); the candidate prefixes of all
+ * requests share one flat slot buffer (Sec. III-C, Flat-buffer packer);
+ * attention runs on a short verification tile matched to the candidate width,
+ * with a separate wide tile for prefill (Sec. III-B, Path-aware tile router);
+ * the prefix verifier accepts the longest exact-match prefix and takes the
+ * successor from row offset_i + a_i (Sec. III-D, Prefix verifier).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Ownership: every pointer argument is device memory owned by the caller
+ *   (unless documented as host).  The library never allocates or frees and
+ *   keeps no state between calls; workspaces are caller-owned buffers sized by
+ *   the *_workspace_bytes queries and may be reused at a fixed address from
+ *   call to call (Sec. III-D, fixed-address workspace).
+ * - Execution: work is enqueued on `stream` and returns without waiting.
+ *   DSV_OK means "validated and enqueued".  There is no host synchronisation
+ *   and no device-to-host readback inside any call (Sec. II-C: no per-step
+ *   host readback for slice reconstruction).
+ * - Host-detectable errors (null required pointer, sizes out of range,
+ *   unsupported head configuration, workspace too small) return a non-zero
+ *   dsv_status before anything is enqueued.
+ * - Data-dependent errors are reported in the caller's device word `status`
+ *   (int32, OR-ed with the DSV_STATUS_* bits below; the library never clears
+ *   it) and the affected outputs take the defined values stated per call.
+ * - Calls are re-entrant; calls that share output or workspace buffers must
+ *   be ordered by the caller (same stream).  No C++ exception crosses the ABI.
+ */
+#ifndef DSV_H
+#define DSV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dsv_status {
+  DSV_OK = 0,
+  DSV_ERR_INVALID_ARG = 1, /* null required pointer, size or layout out of range */
+  DSV_ERR_UNSUPPORTED = 2, /* head_dim / grouping / dtype the kernels do not cover */
+  DSV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the query reports */
+  DSV_ERR_HIP = 4          /* a HIP launch failed */
+} dsv_status;
+
+typedef enum dsv_dtype {
+  DSV_BF16 = 0, /* bfloat16 storage, fp32 arithmetic */
+  DSV_F32 = 1   /* float32 storage and arithmetic */
+} dsv_dtype;
+
+/* Bits of the device status word. */
+#define DSV_STATUS_BAD_REQUEST 1 /* k_i outside [0, W], negative context/base, offsets out of range */
+#define DSV_STATUS_BUDGET 2      /* sum of k_i exceeds the slot capacity m_bs */
+#define DSV_STATUS_NAN 4         /* a NaN logit */
+#define DSV_STATUS_POOL 8        /* a visible KV row or a candidate write outside the pool, or a
+                                    context longer than the split plan (max_ctx) allows */
+#define DSV_STATUS_PREFILL 16    /* a prefill request outside its declared bounds */
+
+/* Largest candidate block width (anchor included) the verification tile covers. */
+#define DSV_MAX_W 16
+
+/* Human-readable name of a status code (static string). */
+const char *dsv_status_string(dsv_status s);
+
+/* ABI version of this header; bumps on any change of a struct or signature. */
+#define DSV_ABI_VERSION 1
+int dsv_abi_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* dsv_pack_slots -- flat-buffer packer                                      */
+/*                                                                            */
+/* DScale Sec. III-C ("Flat-buffer packer", Fig. 6) and Sec. II-C            */
+/* (Challenge 3): prefixes of lengths k_i share one buffer of capacity m_bs  */
+/* using exclusive prefix-sum offsets, and tokens, positions and cache       */
+/* references are packed with identical row mappings.                        */
+/*                                                                            */
+/* Inputs  k[n_bs] (0 = inactive request), ctx_len[n_bs] (committed context), */
+/*         kv_base[n_bs] (first pool row of the request's contiguous KV      */
+/*         segment), block_tokens[n_bs][W] (row-major; column 0 = anchor).   */
+/* Outputs offsets[n_bs + 1]: offsets[i] = sum_{j<i} k_j, offsets[n_bs] = end */
+/*         boundary S.  For slot s = offsets[i] + j (j < k_i):               */
+/*           slot_req[s] = i, slot_tok[s] = block_tokens[i][j],              */
+/*           slot_pos[s] = ctx_len[i] + j,                                    */
+/*           slot_cache_loc[s] = kv_base[i] + ctx_len[i] + j.                */
+/*         Tail slots s in [S, m_bs): req -1, tok 0, pos 0, cache_loc -1.    */
+/* Sizes   0 <= n_bs <= 1048576, 1 <= W <= DSV_MAX_W, 0 <= m_bs < 2^31.     */
+/* Errors  (device) a request with k_i outside [0, W] or negative ctx/base   */
+/*         sets DSV_STATUS_BAD_REQUEST and is packed as inactive (k_i = 0);  */
+/*         if the remaining lengths sum above m_bs, DSV_STATUS_BUDGET is set */
+/*         and every request is packed as inactive (all offsets 0, every     */
+/*         slot a tail placeholder).                                         */
+/* One kernel launch (a single workgroup).                                   */
+/* ------------------------------------------------------------------------ */
+dsv_status dsv_pack_slots(int32_t n_bs, int32_t W, int32_t m_bs, const int32_t *k,
+                          const int32_t *ctx_len, const int64_t *kv_base,
+                          const int32_t *block_tokens, int32_t *offsets, int32_t *slot_req,
+                          int32_t *slot_tok, int32_t *slot_pos, int64_t *slot_cache_loc,
+                          int32_t *status, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* dsv_verify_attn -- tile-routed attention over packed slots                */
+/*                                                                            */
+/* DScale Sec. III-B (Path-aware tile router: verification rows, at most     */
+/* W = 16 per request, use a 16-row tile; prefill keeps a wide tile for KV   */
+/* reuse) and Sec. III-D (valid rows read offset_i + j with request-local    */
+/* causal masking and the supplied cache references).                        */
+/*                                                                            */
+/* Verification set.  Request i has k_i query rows at slots offsets[i] + j.  */
+/* Its key sequence is ctx_len[i] committed rows (pool rows kv_base[i] + p)  */
+/* followed by its k_i candidates (anchor first).  Query row j, for every    */
+/* query head h, attends to positions 0 .. ctx_len[i] + j with KV head       */
+/* h / (hq / hkv):                                                            */
+/*   out = softmax(scale * q K^T) V,  lse = ln sum exp(scale * q K^T).       */
+/* If k_new/v_new are given they hold the candidates' keys and values (row   */
+/* offsets[i] + j); they are used for the candidate positions and written   */
+/* to pool rows slot_cache_loc[offsets[i] + j] (this step's KV writes).  If  */
+/* they are null the candidates are read from pool rows kv_base[i] +         */
+/* ctx_len[i] + j.                                                           */
+/*                                                                            */
+/* Prefill set (optional, n_pf > 0).  Request r has pf_q_len[r] query rows   */
+/* at rows pf_q_start[r] + j of pf_q at positions pf_ctx_len[r] + j; every   */
+/* key/value row (pool rows pf_kv_base[r] + p) must already be in the pool,  */
+/* or be given in pf_k_new/pf_v_new rows pf_q_start[r] + j, which are then   */
+/* written to pool rows pf_kv_base[r] + pf_ctx_len[r] + j first.  Row j      */
+/* attends to positions 0 .. pf_ctx_len[r] + j.                              */
+/*                                                                            */
+/* Layouts (row-major, contiguous unless strided):                           */
+/*   k_pool, v_pool [hkv][pool_rows][d] addressed as                         */
+/*     g * stride_head + row * stride_row + c   (elements; stride_row >= d,  */
+/*     both strides multiples of 8 for bf16 and of 4 for fp32)               */
+/*   q, out [m_bs][hq][d]; k_new, v_new [m_bs][hkv][d]; lse [m_bs][hq] f32   */
+/*   pf_q, pf_out [pf_q_rows][hq][d]; pf_k_new, pf_v_new [pf_q_rows][hkv][d] */
+/*   All of q/out/pool/k_new/v_new/pf_* have element type `dtype`.          */
+/* Outputs: rows of valid requests are written; tail rows                    */
+/*   [offsets[n_bs], m_bs) are zero-filled (lse -inf); any other row is not   */
+/*   touched.  The pool is written only at the candidate (and pf_k_new) rows. */
+/* Supported: d in {64, 128, 256}; hq % hkv == 0; hq / hkv <= 16 (bf16);     */
+/*   W <= DSV_MAX_W.                                                          */
+/* Errors (device): invalid request (k_i outside [0, W], negative ctx/base,  */
+/*   offsets[i] + k_i > m_bs, segment past pool_rows, ctx_len[i] > max_ctx): */
+/*   DSV_STATUS_BAD_REQUEST or DSV_STATUS_POOL, its rows are zero-filled     */
+/*   when its offsets are in range; a candidate write outside the pool is    */
+/*   skipped with DSV_STATUS_POOL; invalid prefill request:                  */
+/*   DSV_STATUS_PREFILL, nothing computed for it.                            */
+/* ------------------------------------------------------------------------ */
+typedef struct dsv_attn_args {
+  dsv_dtype dtype;
+  int32_t hq, hkv, d;
+  float softmax_scale; /* 0 => 1 / sqrt(d) */
+  int32_t kv_chunk;    /* KV rows per split of a verification request (multiple of 64); 0 => auto */
+  int32_t max_ctx;     /* host-known upper bound of every ctx_len[i] of the verification set */
+
+  /* KV pool (written at candidate rows) */
+  void *k_pool, *v_pool;
+  int64_t pool_rows, stride_head, stride_row;
+
+  /* verification set (packed by dsv_pack_slots) */
+  int32_t n_bs, m_bs, W;
+  const int32_t *offsets;        /* [n_bs + 1] */
+  const int32_t *k;              /* [n_bs] */
+  const int32_t *ctx_len;        /* [n_bs] */
+  const int64_t *kv_base;        /* [n_bs] */
+  const int64_t *slot_cache_loc; /* [m_bs], required when k_new is given */
+  const void *q;                 /* [m_bs][hq][d] */
+  const void *k_new, *v_new;     /* [m_bs][hkv][d] or null */
+  void *out;                     /* [m_bs][hq][d] */
+  float *lse;                    /* [m_bs][hq] or null */
+
+  /* prefill set (n_pf = 0 to omit) */
+  int32_t n_pf, pf_max_len, pf_q_rows;
+  const int32_t *pf_q_start, *pf_q_len, *pf_ctx_len; /* [n_pf] */
+  const int64_t *pf_kv_base;                         /* [n_pf] */
+  const void *pf_q;
+  const void *pf_k_new, *pf_v_new; /* or null */
+  void *pf_out;
+  float *pf_lse; /* or null */
+
+  void *workspace;
+  size_t workspace_bytes;
+  int32_t *status;
+
+  /* Optional instrumentation: when non-null, hipEventRecord is called on
+     these events on `stream` immediately before and after the verification
+     attention kernel (the split-KV merge, if any, comes after main_end). */
+  hipEvent_t main_begin, main_end;
+} dsv_attn_args;
+
+/* sizeof(dsv_attn_args) as compiled into the library (binding check). */
+size_t dsv_attn_args_size(void);
+
+/* Workspace bytes dsv_verify_attn needs for these arguments (sizes only are
+   read; pointers may be null).  Returns 0 when none is needed. */
+size_t dsv_verify_attn_workspace_bytes(const dsv_attn_args *args);
+
+dsv_status dsv_verify_attn(const dsv_attn_args *args, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* dsv_accept -- greedy prefix verifier, output builder and draft margin     */
+/*                                                                            */
+/* DScale Sec. III-D (Prefix verifier, greedy: a deterministic top-1 draft   */
+/* is accepted when it equals the target's choice; after a_i accepted        */
+/* candidates, row offset_i + a_i supplies the successor; the output is the  */
+/* accepted candidates followed by the successor), Sec. II-B (progress = one */
+/* anchor plus accepted drafts; the Top1-Top2 draft logit gap, Fig. 4) and   */
+/* DFlash-Mini-Lab (the anchor is not drafted; accept the exact prefix; the  */
+/* top-1/top-2 draft margin of DFlash7-ACT).                                 */
+/*                                                                            */
+/* Target part (target_logits non-null), logits [m_bs][vocab] f32:          */
+/*   slot_argmax[s] = first index of the maximum of row s for s < S =        */
+/*     offsets[n_bs] (-0.0 == +0.0), -1 for s >= S.                          */
+/*   For request i with k_i > 0: a_i = largest a <= k_i - 1 such that        */
+/*     slot_tok[off_i + j] == slot_argmax[off_i + j - 1] for all 1 <= j <= a; */
+/*     accepted[i] = a_i, bonus[i] = slot_argmax[off_i + a_i],               */
+/*     progress[i] = 1 + a_i, out_tokens[i] = the a_i accepted drafts, then  */
+/*     bonus, then -1 up to W.  k_i = 0: accepted 0, bonus -1, progress 0,   */
+/*     out_tokens all -1.                                                     */
+/* Draft part (draft_logits non-null), draft_logits [n_bs][n_pos][draft_vocab] */
+/*   f32: margin[i][p] = fp32(top1 - top2) where top2 is the second element */
+/*   of the row sorted descending as a multiset; draft_top1[i][p] = first    */
+/*   index of top1 (draft_top1 may be null).                                 */
+/* Sizes: 1 <= W <= DSV_MAX_W, vocab >= 1, draft_vocab >= 2, n_pos >= 1.     */
+/* Errors (device): invalid k_i/offsets: DSV_STATUS_BAD_REQUEST, accepted -1, */
+/*   bonus -1, progress 0, out_tokens -1; a NaN in a row: DSV_STATUS_NAN,    */
+/*   that row's argmax / draft_top1 = -1 and its margin NaN.                 */
+/* ------------------------------------------------------------------------ */
+size_t dsv_accept_workspace_bytes(int32_t m_bs, int32_t vocab, int32_t n_bs, int32_t n_pos,
+                                  int32_t draft_vocab);
+
+dsv_status dsv_accept(int32_t n_bs, int32_t m_bs, int32_t W, int32_t vocab,
+                      const float *target_logits, const int32_t *slot_tok, const int32_t *offsets,
+                      const int32_t *k, int32_t *slot_argmax, int32_t *accepted, int32_t *bonus,
+                      int32_t *progress, int32_t *out_tokens, const float *draft_logits,
+                      int32_t n_pos, int32_t draft_vocab, float *margin, int32_t *draft_top1,
+                      void *workspace, size_t workspace_bytes, int32_t *status,
+                      hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSV_H */

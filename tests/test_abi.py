@@ -1,0 +1,77 @@
+"""CPU checks of the C ABI: the library loads (no GPU needed to dlopen it) and exports every
+function include/*.h declares, and the binding's struct matches the library's."""
+import ctypes
+import glob
+import os
+import re
+
+import block_verification_attention_amd as dsv
+from block_verification_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"\b(dsv_[a-z0-9_]+)\s*\(", text):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    dsv.load_library()
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    declared = _declared_functions()
+    assert {"dsv_pack_slots", "dsv_verify_attn", "dsv_accept"} <= declared
+    for name in sorted(declared):
+        assert hasattr(lib, name), f"{name} declared in include/ but not exported"
+
+
+def test_struct_layout_and_version():
+    lib = _lib.load()
+    assert lib.dsv_attn_args_size() == ctypes.sizeof(_lib.AttnArgs)
+    assert lib.dsv_abi_version() == 1
+    assert _lib.status_string(0) == "ok"
+    assert "workspace" in _lib.status_string(3)
+
+
+def test_host_validation_without_gpu():
+    """Host-detectable errors return before anything is enqueued (no GPU is touched)."""
+    lib = _lib.load()
+    st = ctypes.c_int32(0)
+    # W out of range
+    assert lib.dsv_pack_slots(1, 17, 4, None, None, None, None, ctypes.byref(st), None, None, None,
+                              None, ctypes.byref(st), None) == 1
+    a = _lib.AttnArgs()
+    a.dtype = 0
+    a.d = 96  # unsupported head_dim
+    a.hq = a.hkv = 1
+    a.status = ctypes.addressof(st)
+    assert lib.dsv_verify_attn(ctypes.byref(a), None) == 2
+    a.d = 128
+    a.hq, a.hkv = 34, 2  # G = 17 > 16
+    assert lib.dsv_verify_attn(ctypes.byref(a), None) == 2
+    a.hq, a.hkv = 3, 2
+    assert lib.dsv_verify_attn(ctypes.byref(a), None) == 1
+    # accept: missing workspace for a real sweep
+    assert lib.dsv_accept(1, 4, 16, 100, ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16),
+                          ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16),
+                          ctypes.c_void_p(16), ctypes.c_void_p(16), None, None, 0, 0, None, None,
+                          None, 0, ctypes.byref(st), None) == 3
+    assert st.value == 0
+
+
+def test_workspace_queries():
+    lib = _lib.load()
+    assert lib.dsv_accept_workspace_bytes(128, 151936, 0, 0, 0) > 0
+    assert lib.dsv_accept_workspace_bytes(0, 0, 32, 15, 248320) > 0
+    a = _lib.AttnArgs()
+    a.dtype, a.hq, a.hkv, a.d = 0, 32, 8, 128
+    a.n_bs, a.m_bs, a.W, a.max_ctx = 8, 128, 16, 8192
+    n = lib.dsv_verify_attn_workspace_bytes(ctypes.byref(a))
+    assert n > 0 and n % 256 == 0
+    a.max_ctx = 16  # one split: no workspace
+    assert lib.dsv_verify_attn_workspace_bytes(ctypes.byref(a)) == 0

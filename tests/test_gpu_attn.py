@@ -1,0 +1,163 @@
+"""GPU parity of dsv_verify_attn (verification path) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+import oracle  # noqa: E402
+import workloads as wl  # noqa: E402
+from gpu_util import (DEV, bits_of, compare_attn, device_case, gpu_attn, gpu_pack,  # noqa: E402
+                      oracle_attn, oracle_pack, small_case, to_dev, to_f64)
+import block_verification_attention_amd as dsv  # noqa: E402
+
+
+def _run(c, *, use_new=True, kv_chunk=0, tag=""):
+    d = device_case(c)
+    packed = gpu_pack(c, d)
+    ref_pack = oracle_pack(c)
+    assert np.array_equal(packed["offsets"].cpu().numpy(), ref_pack["offsets"])
+    out, lse = gpu_attn(c, d, packed, use_new=use_new, kv_chunk=kv_chunk)
+    torch.cuda.synchronize()
+    assert int(d["status"].item()) == 0
+    ref_out, ref_lse = oracle_attn(c, ref_pack["offsets"], use_new=use_new)
+    w = compare_attn(c, ref_pack["offsets"], out, lse, ref_out, ref_lse, tag=tag or c["name"])
+    return d, packed, out, lse, w
+
+
+def test_config1_fp32():
+    _run(wl.config1(), tag="cfg1")
+
+
+@pytest.mark.parametrize("d_head,hq,hkv", [(64, 4, 1), (128, 8, 2), (128, 32, 8), (256, 24, 2),
+                                            (128, 12, 4), (256, 4, 4)])
+@pytest.mark.parametrize("kv_chunk", [0, 64, 256])
+def test_bf16_ragged(d_head, hq, hkv, kv_chunk):
+    c = small_case(10 + d_head + hq, hq=hq, hkv=hkv, d=d_head,
+                   k=(16, 5, 0, 11, 1, 16, 3), ctx=(700, 0, 40, 63, 64, 1000, 129))
+    _run(c, kv_chunk=kv_chunk, tag=f"d{d_head} hq{hq} hkv{hkv} chunk{kv_chunk}")
+
+
+@pytest.mark.parametrize("d_head", [64, 128, 256])
+def test_fp32_small(d_head):
+    c = small_case(31 + d_head, dtype="f32", hq=4, hkv=2, d=d_head, k=(4, 0, 16, 1), ctx=(50, 3, 0, 300))
+    _run(c)
+
+
+def test_pool_candidates_without_k_new():
+    c = small_case(41, k=(7, 16, 2), ctx=(100, 0, 500))
+    _run(c, use_new=False, kv_chunk=128)
+
+
+def test_sharp_and_sentinel():
+    base = small_case(42, hq=16, hkv=4, d=128, k=(16, 9, 4, 1), ctx=(1000, 20, 333, 0))
+    _run(wl.sharp_variant(base), tag="sharp")
+    _run(wl.sentinel_variant(base), kv_chunk=256, tag="sentinel")
+    _run(wl.sentinel_variant(wl.sharp_variant(base)), tag="sentinel+sharp")
+
+
+def test_candidate_kv_written_at_cache_refs():
+    c = small_case(43, k=(5, 0, 16), ctx=(10, 7, 200))
+    d, packed, *_ = _run(c)
+    ref_k, ref_v = oracle.scatter_candidates(c["k_pool"], c["v_pool"], c["k_new"], c["v_new"],
+                                             oracle_pack(c)["slot_cache_loc"])
+    assert np.array_equal(bits_of(d["k_pool"]), ref_k)
+    assert np.array_equal(bits_of(d["v_pool"]), ref_v)
+
+
+def test_packed_equals_padded_and_deterministic():
+    """Same requests launched packed and padded (each request owns W rows, gaps between
+    them): valid rows are bit-identical with the split size pinned; two runs agree bitwise."""
+    c = small_case(44, hq=8, hkv=2, d=128, k=(3, 16, 7, 1), ctx=(300, 64, 0, 1025), extra_tail=0)
+    d = device_case(c)
+    packed = gpu_pack(c, d)
+    o1, l1 = gpu_attn(c, d, packed, use_new=False, kv_chunk=128)
+    o2, l2 = gpu_attn(c, d, packed, use_new=False, kv_chunk=128)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    n, W = c["n_bs"], c["W"]
+    off = packed["offsets"].cpu().numpy()
+    q_pad = torch.zeros((n * W, c["hq"], c["d"]), dtype=torch.bfloat16, device=DEV)
+    for i in range(n):
+        q_pad[i * W:i * W + c["k"][i]] = d["q"][off[i]:off[i] + c["k"][i]]
+    pad_off = torch.arange(0, n * W + 1, W, dtype=torch.int32, device=DEV)
+    cp = dict(c, m_bs=n * W)
+    dp = dict(d, q=q_pad)
+    out_pad = torch.full_like(q_pad, float("nan"))
+    op, lp = gpu_attn(cp, dp, packed, use_new=False, kv_chunk=128, out=out_pad, offsets=pad_off)
+    torch.cuda.synchronize()
+    for i in range(n):
+        kk = int(c["k"][i])
+        assert torch.equal(op[i * W:i * W + kk].view(torch.int16), o1[off[i]:off[i] + kk].view(torch.int16))
+        assert torch.equal(lp[i * W:i * W + kk], l1[off[i]:off[i] + kk])
+        # gap rows of the padded layout are not touched
+        assert torch.isnan(op[i * W + kk:(i + 1) * W].float()).all()
+
+
+def test_config2_two_steps_layout_shift():
+    """Step 1 [4,12,8] then step 2 [10,8,6] in the same pool: step 1's candidates are written
+    at their cache references, the committed prefix (anchor + accepted drafts) becomes step 2's
+    context, and step 2's new boundaries never mix requests."""
+    s1, s2 = wl.config2()
+    d1 = device_case(s1)
+    p1 = gpu_pack(s1, d1)
+    o1, l1 = gpu_attn(s1, d1, p1)
+    torch.cuda.synchronize()
+    ref1 = oracle_pack(s1)
+    r1o, r1l = oracle_attn(s1, ref1["offsets"])
+    compare_attn(s1, ref1["offsets"], o1, l1, r1o, r1l, tag="cfg2 step1")
+    # oracle's view of the pool after step 1
+    kp, vp = oracle.scatter_candidates(s1["k_pool"], s1["v_pool"], s1["k_new"], s1["v_new"],
+                                       ref1["slot_cache_loc"])
+    # step 2 runs on the device pool step 1 wrote
+    d2 = device_case(s2)
+    d2["k_pool"], d2["v_pool"] = d1["k_pool"], d1["v_pool"]
+    p2 = gpu_pack(s2, d2)
+    o2, l2 = gpu_attn(s2, d2, p2)
+    torch.cuda.synchronize()
+    assert int(d1["status"].item()) == 0 and int(d2["status"].item()) == 0
+    ref2 = oracle_pack(s2)
+    assert list(ref1["offsets"]) == [0, 4, 16, 24] and list(ref2["offsets"]) == [0, 10, 18, 24]
+    r2o, r2l = oracle_attn(s2, ref2["offsets"], k_pool=kp, v_pool=vp)
+    compare_attn(s2, ref2["offsets"], o2, l2, r2o, r2l, tag="cfg2 step2")
+
+
+def test_config3_full():
+    c = wl.config3(with_logits=False)
+    _run(c, tag="cfg3")
+
+
+def test_config4_full():
+    c = wl.config4(with_draft_logits=False)
+    _run(c, tag="cfg4")
+
+
+def test_invalid_requests_flagged_and_zeroed():
+    c = small_case(45, k=(4, 6, 3), ctx=(10, 20, 30))
+    d = device_case(c)
+    packed = gpu_pack(c, d)
+    # request 1's segment pushed past the pool; request 2 claims k > W
+    kb = d["kv_base"].clone()
+    kb[1] = c["pool_rows"] - 5
+    d2 = dict(d, kv_base=kb)
+    k_bad = d["k"].clone()
+    k_bad[2] = 17
+    out, lse = gpu_attn(c, d2, packed, k=k_bad)
+    torch.cuda.synchronize()
+    st = int(d["status"].item())
+    assert st & dsv.STATUS_POOL and st & dsv.STATUS_BAD_REQUEST
+    off = packed["offsets"].cpu().numpy()
+    assert torch.all(out[off[1]:off[1] + 6] == 0)
+    assert torch.isfinite(out[off[0]:off[0] + 4].float()).all()
+    # request 2 (k > W) has out-of-range k: its rows are left untouched
+    assert torch.isnan(out[off[2]:off[2] + 3].float()).all()
+
+
+def test_max_ctx_plan_exceeded_is_flagged():
+    c = small_case(46, k=(4, 4), ctx=(900, 100))
+    d = device_case(c)
+    packed = gpu_pack(c, d)
+    out, _ = gpu_attn(c, d, packed, kv_chunk=64, max_ctx=500)
+    torch.cuda.synchronize()
+    assert int(d["status"].item()) & dsv.STATUS_POOL
+    assert torch.all(out[0:4] == 0)
+    assert torch.isfinite(out[4:8].float()).all()
