@@ -7,6 +7,7 @@ The library has no PyTorch dependency: it links only the HIP runtime.
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 
@@ -36,22 +37,59 @@ def hipcc() -> str:
     return "hipcc"
 
 
+# attn_bf16_kernel<D, NW, PF, TILE, NSTAGE, DEEP>
+_ATTN_KERNEL = re.compile(r"attn_bf16_kernelILi(\d+)ELi(\d+)ELb([01])ELi(\d+)ELi(\d+)ELb([01])E")
+
+
+def check_deep_kernels_without_scratch(remarks: str) -> int:
+    """The multi-stage schedule of the attention kernel counts its own outstanding loads;
+    a register spill (scratch access) inside that window would break the count.  Every
+    instantiation compiled with that schedule must therefore use no scratch.  Returns the
+    number of such kernels checked; raises if one uses scratch."""
+    checked = 0
+    current = None
+    for line in remarks.splitlines():
+        if "Function Name:" in line:
+            m = _ATTN_KERNEL.search(line)
+            current = m if (m and m.group(6) == "1") else None
+        elif current is not None and "ScratchSize [bytes/lane]:" in line:
+            size = int(line.rsplit(":", 1)[1].split()[0])
+            if size != 0:
+                d, nw = current.group(1), current.group(2)
+                raise RuntimeError(f"attention kernel D={d} waves={nw} (multi-stage schedule) uses "
+                                   f"{size} B/lane of scratch; move it to the conservative schedule")
+            checked += 1
+            current = None
+    return checked
+
+
 def build(verbose: bool = False) -> str:
     """Compiles every source and links libdsv.so; always rebuilds.  Returns the path."""
     objs = []
     build_dir = os.path.join(PKG, "_build")
     os.makedirs(build_dir, exist_ok=True)
+    procs = []
     for src in SOURCES:
         obj = os.path.join(build_dir, src.replace(".hip", ".o"))
         cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj]
+        if src == "dsv_attn.hip":
+            cmd.append("-Rpass-analysis=kernel-resource-usage")
         if verbose:
             print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
+        procs.append((src, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+    for src, obj, proc in procs:
+        out, err = proc.communicate()
         # hipcc's host pass reports the device-only target feature as unknown: harmless
         noise = "is not a recognized feature for this target"
-        msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)
-        if r.returncode != 0:
-            raise RuntimeError(f"hipcc failed on {src}:\n{msg}")
+        lines = [l for l in (out + err).splitlines() if noise not in l]
+        if proc.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n" + "\n".join(lines))
+        if src == "dsv_attn.hip":
+            n = check_deep_kernels_without_scratch("\n".join(lines))
+            if n == 0:
+                raise RuntimeError("no multi-stage attention kernel found in the resource report")
+            lines = [l for l in lines if "remark:" not in l and "kernel-resource-usage" not in l]
+        msg = "\n".join(lines)
         if msg.strip() and verbose:
             print(msg)
         objs.append(obj)

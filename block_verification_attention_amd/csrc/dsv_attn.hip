@@ -33,11 +33,13 @@
 //                keeps both the transposing writes and the operand reads conflict-free.
 #include <math.h>
 
+#include <type_traits>
+
 #include "dsv_internal.h"
 
 namespace dsv {
 
-constexpr int kTileKV = 64;
+constexpr int kTileKV = 64;  // split granularity (multiple of every tile height)
 constexpr int kPfWaves = 8;  // 8 waves x 16 rows = 128-row prefill tile
 constexpr int kPfRows = kPfWaves * 16;
 
@@ -92,15 +94,6 @@ __device__ __forceinline__ int prefill_request(const AttnParams &p, int r, int &
   return 0;
 }
 
-__device__ __forceinline__ int vt_swz(int d) { return ((d >> 3) + 2 * (d & 7)) & 15; }
-
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
-  return (a & 0xffffu) | (b << 16);
-}
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xffff0000u);
-}
-
 // Zero-fills rows [r0, r1) of a [rows][hq][D] bf16 tensor for heads [h0, h0 + nh), lse -inf.
 template <int D>
 __device__ void zero_rows_bf16(uint16_t *out, float *lse, int hq, int r0, int r1, int h0, int nh,
@@ -120,31 +113,150 @@ __device__ void zero_rows_bf16(uint16_t *out, float *lse, int hq, int r0, int r1
 }
 
 // ---------------------------------------------------------------------------
+// Direct global->LDS loads.  Each lane of a wave moves 16 bytes; the wave's 64 x 16 B land
+// contiguously at the wave-uniform LDS address in m0, so the XOR swizzle of the tile is
+// applied on the global side (each lane picks which 16-byte column slot of its row it
+// fetches).  Completion is tracked with vmcnt, waited for explicitly: the compiler would
+// otherwise wait for every outstanding LDS load before each barrier, which collapses the
+// multi-stage ring to a single stage.
+// Interior tiles use a buffer descriptor over the request's KV segment with a lane-constant
+// VGPR offset and a per-tile scalar offset (no per-tile vector address arithmetic);
+// boundary tiles (candidate rows from k_new, rows past the range) use per-lane addresses.
+// ---------------------------------------------------------------------------
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void lds_dma16(uint32_t lds_wave_base, const void *src) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_wave_base), "v"(src)
+               : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+__device__ __forceinline__ void lds_dma16_buf(uint32_t lds_wave_base, i32x4 rsrc_in, uint32_t voff,
+                                              uint32_t soff) {
+  i32x4 rsrc;  // the descriptor must live in scalar registers
+  rsrc[0] = __builtin_amdgcn_readfirstlane(rsrc_in[0]);
+  rsrc[1] = __builtin_amdgcn_readfirstlane(rsrc_in[1]);
+  rsrc[2] = __builtin_amdgcn_readfirstlane(rsrc_in[2]);
+  rsrc[3] = __builtin_amdgcn_readfirstlane(rsrc_in[3]);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_wave_base), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+// Raw buffer descriptor (stride 0, 32-bit byte offsets) over [base, base + bytes).
+__device__ __forceinline__ i32x4 buffer_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Waits until this wave's loads of every tile issued before the last `after` tiles are
+// complete (per tile each wave issues at least PER loads).  vmcnt holds at most 63; a larger
+// count is clamped, which only waits a little longer than needed.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_clamped() {
+  wait_vmcnt<(N > 63 ? 63 : N)>();
+}
+template <int PER, int NSTAGE>
+__device__ __forceinline__ void wait_tiles(int after) {
+  if (NSTAGE > 3 && after >= 3) wait_vmcnt_clamped<PER * 3>();
+  else if (NSTAGE > 2 && after >= 2) wait_vmcnt_clamped<PER * 2>();
+  else if (NSTAGE > 1 && after >= 1) wait_vmcnt_clamped<PER>();
+  else wait_vmcnt<0>();
+}
+
+// LDS tile layouts: row-major [TILE][D] bf16 for both K and V, 16-byte column slots permuted
+// per row.  K: slot ^ (row & 15) -- the 16 rows of an MFMA operand read (one slot each) land
+// in distinct banks.  V: slot ^ 2*(row & 7) (a permutation of 32-byte blocks) -- the four
+// rows x 32 bytes that a 16-lane group touches in a transposing read land in distinct banks.
+template <int D>
+__device__ __forceinline__ int k_slot(int row, int slot) {
+  constexpr int SW = (D / 8) < 16 ? (D / 8) : 16;
+  return slot ^ (row & (SW - 1));
+}
+template <int D>
+__device__ __forceinline__ int v_slot(int row, int slot) {
+  constexpr int VB = D / 16;  // 32-byte blocks per row
+  constexpr int M = VB < 8 ? VB : 8;
+  return slot ^ (2 * (row & (M - 1)));
+}
+
+typedef __attribute__((address_space(3))) uint4 lds_u4;
+typedef __bf16 bf16x4v __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef __attribute__((address_space(3))) bf16x4v lds_bf16x4;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// Lazy reference-max threshold (log2 units): the softmax reference only moves when a tile's
+// maximum exceeds it by more than this, so the probabilities stay below 2^8 and the output
+// accumulators are rarely rescaled.  The result is unchanged: numerator and denominator use
+// the same reference.
+constexpr float kRescaleSlack = 8.0f;
+
+// ---------------------------------------------------------------------------
 // bf16 MFMA attention kernel.  PF = false: verification (NW = G waves, one 16-row query
 // tile per query head, split KV).  PF = true: prefill (NW = 8 waves along the query rows of
-// one head).
+// one head).  KV tiles of TILE rows stream through an NSTAGE-deep LDS ring.
 // ---------------------------------------------------------------------------
-template <int D, int NW, bool PF>
-__global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnParams p) {
-  constexpr int NT = NW * 64;
-  constexpr int KCH = D / 8;                    // 16-byte chunks per row
-  constexpr int SW = KCH < 16 ? KCH : 16;       // K swizzle period
-  constexpr int NKC = kTileKV * KCH;            // K chunks per tile
-  constexpr int NVB = (kTileKV / 4) * KCH;      // V blocks (4 rows x 8 columns) per tile
-  constexpr int KPT = (NKC + NT - 1) / NT;
-  constexpr int VPT = (NVB + NT - 1) / NT;
+// Schedules.  DEEP: NSTAGE - 1 tiles in flight while one is consumed; the wait counts this
+// wave's own loads exactly, which is only valid when no other vector-memory instruction (such
+// as a register spill) can sit between the loads and the wait -- the build checks that every
+// DEEP instantiation uses no scratch.  Otherwise: wait for everything, then issue the next
+// tile and compute the current one (one tile in flight during the computation).
+// DEEP is limited to workgroups of 3..8 waves with head_dim <= 128 (2..16 waves for 64): those
+// keep at most 32 of their own loads in flight per wave and fit the register file without
+// spilling into accumulation registers.  Single- and two-wave workgroups with 128-wide rows
+// and every head_dim-256 shape use the conservative schedule.
+template <int D, int NW>
+constexpr bool deep_schedule() {
+  return (D == 64 && NW >= 2) || (D == 128 && NW >= 3 && NW <= 8);
+}
+template <int D, int NW>
+constexpr int waves_per_eu_hint() {
+  // small workgroups get the whole register file; 3..8 waves are asked to fit 2 waves/SIMD
+  return (NW <= 2 || (D == 256 && NW <= 4)) ? 1 : (NW <= 8 ? 2 : 1);
+}
+
+template <int D, int NW, bool PF, int TILE, int NSTAGE, bool DEEP>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_per_eu_hint<D, NW>()))) void attn_bf16_kernel(AttnParams p) {
+  constexpr int RPC = 1024 / (2 * D);        // rows per 1 KB wave load
+  constexpr int NCK = TILE / RPC;            // wave loads per tensor per tile
+  constexpr int PER = (2 * NCK) / NW;        // wave loads per wave per tile (at least)
+  constexpr int QPW = (2 * NCK + NW - 1) / NW;  // wave loads per wave per tile (at most)
+  constexpr int STAGE_BYTES = 2 * TILE * D * 2;
   constexpr int DB = D / 16;
   constexpr int KS = D / 32;
+  constexpr int KB = TILE / 16;              // 16-row score blocks per tile
+  constexpr int KK = TILE / 32;              // 32-row P.V steps per tile
+  static_assert(TILE % 32 == 0 && TILE % RPC == 0 && PER >= 1, "tile shape");
 
   extern __shared__ __align__(16) uint16_t lds[];
-  uint16_t *sK = lds;
-  uint16_t *sVt = lds + kTileKV * D;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)lds;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int lq = lane & 15, lg = lane >> 4;
-
-  const uint16_t *kpool = static_cast<const uint16_t *>(p.k_pool);
-  const uint16_t *vpool = static_cast<const uint16_t *>(p.v_pool);
 
   // ---- work unit ----
   int g, h, c, r_lo, r_hi, row0, nrows, split = 0, n_splits_i = 1, off = 0;
@@ -162,7 +274,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnParams p) {
       int end = p.offsets[p.n_bs];
       end = end < 0 ? 0 : (end > p.m_bs ? p.m_bs : end);
       zero_rows_bf16<D>(static_cast<uint16_t *>(p.out), p.lse, p.hq, end, p.m_bs, g * p.G, p.G,
-                        tid, NT);
+                        tid, NW * 64);
     }
     int ki;
     const int bad = verify_request(p, i, ki, off, c, kb);
@@ -171,7 +283,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnParams p) {
         if (tid == 0 && g == 0) status_or(p.status, bad);
         if (ki >= 0 && ki <= p.W && off >= 0 && (int64_t)off + ki <= p.m_bs)
           zero_rows_bf16<D>(static_cast<uint16_t *>(p.out), p.lse, p.hq, off, off + ki, g * p.G,
-                            p.G, tid, NT);
+                            p.G, tid, NW * 64);
       }
       return;
     }
@@ -187,6 +299,23 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnParams p) {
     if (p.k_new) {
       knew = static_cast<const uint16_t *>(p.k_new);
       vnew = static_cast<const uint16_t *>(p.v_new);
+      // this step's KV writes: the candidates this split covers go to their cache references
+      const int p0 = max(c, r_lo), p1 = r_hi;
+      constexpr int C16 = D / 8;
+      for (int e = tid; e < (p1 - p0) * C16 * 2; e += NW * 64) {
+        const int isv = e / ((p1 - p0) * C16);
+        const int rem = e % ((p1 - p0) * C16);
+        const int pos = p0 + rem / C16, cc = rem % C16;
+        const int64_t loc = p.slot_cache_loc[off + pos - c];
+        if (loc < 0 || loc >= p.pool_rows) {
+          status_or(p.status, DSV_STATUS_POOL);
+          continue;
+        }
+        const uint16_t *src = (isv ? vnew : knew) + ((int64_t)(off + pos - c) * p.hkv + g) * D + cc * 8;
+        uint16_t *dst = static_cast<uint16_t *>(isv ? p.v_pool : p.k_pool) + g * p.stride_head +
+                        loc * p.stride_row + cc * 8;
+        *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
+      }
     }
   } else {
     const int bid = blockIdx.x;
@@ -224,188 +353,208 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnParams p) {
     }
   }
   const int lim = c + my_row;  // last visible position of this lane's query row
+  // every plain global access above is complete before the LDS loads start
+  __builtin_amdgcn_s_waitcnt(0);
 
-  // ---- KV source of position pos (pool row, or this step's candidate row) ----
-  auto ksrc = [&](int pos) -> const uint16_t * {
-    if (knew && pos >= c)
-      return knew + ((int64_t)(off + pos - c) * p.hkv + g) * D;
-    return kpool + g * p.stride_head + (kb + pos) * p.stride_row;
-  };
-  auto vsrc = [&](int pos) -> const uint16_t * {
-    if (vnew && pos >= c)
-      return vnew + ((int64_t)(off + pos - c) * p.hkv + g) * D;
-    return vpool + g * p.stride_head + (kb + pos) * p.stride_row;
-  };
-  // Candidate rows taken from k_new / v_new are also stored at their cache references.
-  auto kv_dest = [&](int pos) -> int64_t {
-    const int64_t loc = p.slot_cache_loc[off + pos - c];
-    if (loc < 0 || loc >= p.pool_rows) {
-      status_or(p.status, DSV_STATUS_POOL);
-      return -1;
+  // ---- tile loads: wave w issues loads q = w, w + NW, ... of the 2 * NCK per tile ----
+  const int64_t row_elems = p.stride_row;
+  const uint32_t row_bytes = (uint32_t)(row_elems * 2);
+  const uint16_t *kseg = static_cast<const uint16_t *>(p.k_pool) + g * p.stride_head + kb * row_elems;
+  const uint16_t *vseg = static_cast<const uint16_t *>(p.v_pool) + g * p.stride_head + kb * row_elems;
+  // rows [0, n_fast) of the request come from the pool; interior tiles lie below it
+  const int n_fast = knew ? min(r_hi, c) : r_hi;
+  const i32x4 krsrc = buffer_rsrc(kseg, 0xffffffffu);
+  const i32x4 vrsrc = buffer_rsrc(vseg, 0xffffffffu);
+  uint32_t voff[QPW];
+#pragma unroll
+  for (int u = 0; u < QPW; ++u) {
+    const int q = w + u * NW;
+    const bool isv = q >= NCK;
+    const int qq = isv ? q - NCK : q;
+    const int row = qq * RPC + lane / (D / 8);
+    const int slot = lane % (D / 8);
+    voff[u] = row * row_bytes + 16 * (isv ? v_slot<D>(row, slot) : k_slot<D>(row, slot));
+  }
+  auto issue_tile = [&](int tile_base, int stage) __attribute__((always_inline)) {
+    const uint32_t sbase = lds_base + stage * STAGE_BYTES;
+    if (tile_base + TILE <= n_fast) {
+      const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)tile_base * row_bytes);
+#pragma unroll
+      for (int u = 0; u < QPW; ++u) {
+        const int q = w + u * NW;
+        if (q < 2 * NCK) {
+          const bool isv = q >= NCK;
+          const int qq = isv ? q - NCK : q;
+          const uint32_t m0 = __builtin_amdgcn_readfirstlane(sbase + (isv ? TILE * D * 2 : 0) + qq * 1024);
+          lds_dma16_buf(m0, isv ? vrsrc : krsrc, voff[u], soff);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < QPW; ++u) {
+        const int q = w + u * NW;
+        if (q < 2 * NCK) {
+          const bool isv = q >= NCK;
+          const int qq = isv ? q - NCK : q;
+          const int row = qq * RPC + lane / (D / 8);
+          const int slot = lane % (D / 8);
+          int pos = tile_base + row;
+          pos = pos < r_hi ? pos : r_hi - 1;  // rows past the range re-read a visible row (masked)
+          const uint16_t *src;
+          if (knew && pos >= c)
+            src = (isv ? vnew : knew) + ((int64_t)(off + pos - c) * p.hkv + g) * D;
+          else
+            src = (isv ? vseg : kseg) + (int64_t)pos * row_elems;
+          src += 8 * (isv ? v_slot<D>(row, slot) : k_slot<D>(row, slot));
+          const uint32_t m0 = __builtin_amdgcn_readfirstlane(sbase + (isv ? TILE * D * 2 : 0) + qq * 1024);
+          lds_dma16(m0, src);
+        }
+      }
     }
-    return g * p.stride_head + loc * p.stride_row;
   };
 
-  uint4 kreg[KPT];
-  uint4 vreg[VPT][4];
-  auto load_tile = [&](int base) {
+  // ---- lane-constant LDS operand offsets ----
+  // K (A operand of S^T): row 16kb + lq, slot 4ks + lg
+  uint32_t koff[KS];
 #pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int ci = tid + u * NT;
-      kreg[u] = make_uint4(0, 0, 0, 0);
-      if (ci < NKC) {
-        const int row = ci / KCH, col = ci % KCH;
-        const int pos = base + row;
-        if (pos < r_hi) {
-          kreg[u] = *reinterpret_cast<const uint4 *>(ksrc(pos) + col * 8);
-          if (knew && pos >= c) {
-            const int64_t dst = kv_dest(pos);
-            if (dst >= 0)
-              *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.k_pool) + dst + col * 8) = kreg[u];
-          }
-        }
-      }
-    }
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = lds_base + lq * (2 * D) + k_slot<D>(lq, 4 * ks + lg) * 16;
+  // V (transposing reads): row R + lq/4 with R = 32kk + 16half + 4lg, 8 bytes at column
+  // 16db + 4(lq%4); the row term 32kk + 16half does not change the swizzle
+  uint32_t voffs[DB];
 #pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int bi = tid + u * NT;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vreg[u][r] = make_uint4(0, 0, 0, 0);
-      if (bi < NVB) {
-        const int dc = bi % KCH, rg = bi / KCH;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int pos = base + 4 * rg + r;
-          if (pos < r_hi) {
-            vreg[u][r] = *reinterpret_cast<const uint4 *>(vsrc(pos) + dc * 8);
-            if (vnew && pos >= c) {
-              const int64_t dst = kv_dest(pos);
-              if (dst >= 0)
-                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(p.v_pool) + dst + dc * 8) =
-                    vreg[u][r];
-            }
-          }
-        }
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const int ci = tid + u * NT;
-      if (ci < NKC) {
-        const int row = ci / KCH, col = ci % KCH;
-        *reinterpret_cast<uint4 *>(sK + row * D + ((col ^ (row & (SW - 1))) * 8)) = kreg[u];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      const int bi = tid + u * NT;
-      if (bi < NVB) {
-        const int dc = bi % KCH, rg = bi / KCH;
-        const uint32_t *r0 = reinterpret_cast<const uint32_t *>(&vreg[u][0]);
-        const uint32_t *r1 = reinterpret_cast<const uint32_t *>(&vreg[u][1]);
-        const uint32_t *r2 = reinterpret_cast<const uint32_t *>(&vreg[u][2]);
-        const uint32_t *r3 = reinterpret_cast<const uint32_t *>(&vreg[u][3]);
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          // columns d = 8dc + 2e2 (low halves) and 8dc + 2e2 + 1 (high halves)
-          const int d0 = dc * 8 + 2 * e2;
-          uint2 lo = make_uint2(pack_lo(r0[e2], r1[e2]), pack_lo(r2[e2], r3[e2]));
-          uint2 hi = make_uint2(pack_hi(r0[e2], r1[e2]), pack_hi(r2[e2], r3[e2]));
-          *reinterpret_cast<uint2 *>(sVt + d0 * kTileKV + ((rg ^ vt_swz(d0)) * 4)) = lo;
-          *reinterpret_cast<uint2 *>(sVt + (d0 + 1) * kTileKV + ((rg ^ vt_swz(d0 + 1)) * 4)) = hi;
-        }
-      }
-    }
-  };
+  for (int db = 0; db < DB; ++db) {
+    const int row = 4 * lg + (lq >> 2);
+    voffs[db] = lds_base + TILE * D * 2 + row * (2 * D) + v_slot<D>(row, 2 * db + ((lq & 3) >> 1)) * 16 +
+                8 * (lq & 1);
+  }
 
   f32x4 acc_o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc_o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f;  // reference max (log2 units) and row-sum partial
 
-  const int n_tiles = (r_hi - r_lo + kTileKV - 1) / kTileKV;
-  // rows of this wave: PF -> [row0 + 16w, +16); verify -> [0, 16)
+  const int n_tiles = (r_hi - r_lo + TILE - 1) / TILE;
   const int wave_row_lo = PF ? row0 + w * 16 : 0;
   const bool wave_live = wave_row_lo < nrows;
+  const float sl2 = p.scale_log2;
 
-  load_tile(r_lo);
-  for (int t = 0; t < n_tiles; ++t) {
-    const int base = r_lo + t * kTileKV;
-    __syncthreads();  // previous tile's LDS reads are done
-    store_tile();
-    __syncthreads();
-    if (t + 1 < n_tiles) load_tile(base + kTileKV);
-
-    // skip tiles wholly past this wave's last visible position
-    if (!wave_live || base > c + wave_row_lo + 15) continue;
-
-    // S^T blocks: acc_s[kb][e] = score of KV row base + 16kb + 4lg + e for query row lq
-    f32x4 acc_s[4];
+  auto compute_tile = [&](int base, auto stage_c, auto mask_c) __attribute__((always_inline)) {
+    constexpr int STAGE = decltype(stage_c)::value;
+    constexpr bool MASK = decltype(mask_c)::value;
+    // S^T blocks: acc_s[kb][e] = raw score of KV row base + 16kb + 4lg + e for query row lq
+    f32x4 acc_s[KB];
 #pragma unroll
-    for (int kbk = 0; kbk < 4; ++kbk) {
+    for (int kbk = 0; kbk < KB; ++kbk) {
       acc_s[kbk] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t *krow = sK + (16 * kbk + lq) * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int slot = (4 * ks + lg) ^ (lq & (SW - 1));
-        bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(krow + slot * 8));
+        const uint32_t a_addr = koff[ks] + STAGE * STAGE_BYTES + 16 * kbk * (2 * D);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *(lds_u4 *)(uintptr_t)a_addr);
         acc_s[kbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], acc_s[kbk], 0, 0, 0);
       }
     }
-    // scale, mask, tile max
     float mt = -INFINITY;
 #pragma unroll
-    for (int kbk = 0; kbk < 4; ++kbk)
+    for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int pos = base + 16 * kbk + 4 * lg + e;
-        float x = acc_s[kbk][e] * p.scale_log2;
-        x = (pos < r_hi && pos <= lim) ? x : -INFINITY;
-        acc_s[kbk][e] = x;
-        mt = fmaxf(mt, x);
+        if constexpr (MASK) {
+          const int pos = base + 16 * kbk + 4 * lg + e;
+          acc_s[kbk][e] = (pos < r_hi && pos <= lim) ? acc_s[kbk][e] : -INFINITY;
+        }
+        mt = fmaxf(mt, acc_s[kbk][e]);
       }
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-    // P rounded to bf16 is the B operand of O^T = V^T P^T; the row sum (and so the lse)
-    // accumulates the fp32 values
-    uint32_t pb[4][2];
-    float lsum = 0.f;
+    const float mt2 = mt * sl2;  // tile max in log2 units (-inf if fully masked)
+    if (__builtin_expect(__any(mt2 > m_ref + kRescaleSlack), 0)) {
+      const float m_new = mt2 > m_ref + kRescaleSlack ? mt2 : m_ref;
+      // rows that have seen no visible key yet hold zeros: their factor is 0 (not NaN)
+      const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_run *= alpha;
 #pragma unroll
-    for (int kbk = 0; kbk < 4; ++kbk) {
-      uint32_t bits[4];
+      for (int db = 0; db < DB; ++db) acc_o[db] *= alpha;
+    }
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+    // P (bf16) is the B operand of O^T = V^T P^T; the row sum accumulates the fp32 values
+    uint32_t pb[KB][2];
+#pragma unroll
+    for (int kbk = 0; kbk < KB; ++kbk) {
+      float pe[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float pe = __builtin_amdgcn_exp2f(acc_s[kbk][e] - m_use);
-        bits[e] = f32_to_bf16_bits(pe);
-        lsum += pe;
+        pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc_s[kbk][e], sl2, -m_use));
+        l_run += pe[e];
       }
-      pb[kbk][0] = bits[0] | (bits[1] << 16);
-      pb[kbk][1] = bits[2] | (bits[3] << 16);
+      pb[kbk][0] = cvt_pk_bf16(pe[0], pe[1]);
+      pb[kbk][1] = cvt_pk_bf16(pe[2], pe[3]);
     }
-    l_run = l_run * alpha + lsum;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) acc_o[db] *= alpha;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
       const bf16x8 b = __builtin_bit_cast(
           bf16x8, make_uint4(pb[2 * kk][0], pb[2 * kk][1], pb[2 * kk + 1][0], pb[2 * kk + 1][1]));
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int d = 16 * db + lq;
-        const uint16_t *vrow = sVt + d * kTileKV;
-        const int sw = vt_swz(d);
-        const uint2 lo = *reinterpret_cast<const uint2 *>(vrow + (((8 * kk + lg) ^ sw) * 4));
-        const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + (((8 * kk + 4 + lg) ^ sw) * 4));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        // transposing reads: lane j of each 16-lane group receives V[R + t][16db + j], t < 4,
+        // from the 8-byte chunks that lanes j/4 + 4t point at (rows R + lq/4, columns
+        // 16db + 4(lq%4)); R = 32kk + 16half + 4lg.
+        const uint32_t v0 = voffs[db] + STAGE * STAGE_BYTES + (32 * kk) * (2 * D);
+        const auto lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(uintptr_t)v0);
+        const auto hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(uintptr_t)(v0 + 16 * (2 * D)));
+        bf16x8 a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = lo[e];
+          a[4 + e] = hi[e];
+        }
         acc_o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc_o[db], 0, 0, 0);
       }
     }
+  };
+
+  // rows of this wave that can see any key of tile `base`; interior tiles skip the mask
+  auto consume = [&](int base, auto stage_c) __attribute__((always_inline)) {
+    if (!wave_live || base > c + wave_row_lo + 15) return;  // past every row's last position
+    if (base + TILE - 1 <= c + wave_row_lo && base + TILE <= r_hi)
+      compute_tile(base, stage_c, std::integral_constant<bool, false>{});
+    else
+      compute_tile(base, stage_c, std::integral_constant<bool, true>{});
+  };
+  if constexpr (DEEP) {
+#pragma unroll
+    for (int s = 0; s < NSTAGE - 1; ++s)
+      if (s < n_tiles) issue_tile(r_lo + s * TILE, s);
+    auto step = [&](int t, auto stage_c) __attribute__((always_inline)) {
+      constexpr int STAGE = decltype(stage_c)::value;
+      __syncthreads();  // every wave is done with the stage the next load overwrites
+      const int nxt = t + NSTAGE - 1;
+      if (nxt < n_tiles) issue_tile(r_lo + nxt * TILE, (STAGE + NSTAGE - 1) % NSTAGE);
+      wait_tiles<PER, NSTAGE>(min(NSTAGE - 1, n_tiles - 1 - t));
+      __syncthreads();  // tile t is in LDS for every wave
+      consume(r_lo + t * TILE, stage_c);
+    };
+    for (int t0 = 0; t0 < n_tiles; t0 += NSTAGE) {
+      step(t0, std::integral_constant<int, 0>{});
+      if constexpr (NSTAGE > 1) if (t0 + 1 < n_tiles) step(t0 + 1, std::integral_constant<int, 1 % NSTAGE>{});
+      if constexpr (NSTAGE > 2) if (t0 + 2 < n_tiles) step(t0 + 2, std::integral_constant<int, 2 % NSTAGE>{});
+      if constexpr (NSTAGE > 3) if (t0 + 3 < n_tiles) step(t0 + 3, std::integral_constant<int, 3 % NSTAGE>{});
+    }
+  } else {
+    static_assert(NSTAGE == 2, "the conservative schedule double-buffers");
+    issue_tile(r_lo, 0);
+    auto step = [&](int t, auto stage_c) __attribute__((always_inline)) {
+      constexpr int STAGE = decltype(stage_c)::value;
+      wait_vmcnt<0>();   // tile t (and anything else outstanding) is complete
+      __syncthreads();   // ... for every wave, and the other stage is no longer read
+      if (t + 1 < n_tiles) issue_tile(r_lo + (t + 1) * TILE, 1 - STAGE);
+      consume(r_lo + t * TILE, stage_c);
+    };
+    for (int t0 = 0; t0 < n_tiles; t0 += 2) {
+      step(t0, std::integral_constant<int, 0>{});
+      if (t0 + 1 < n_tiles) step(t0 + 1, std::integral_constant<int, 1>{});
+    }
+    wait_vmcnt<0>();
   }
 
   if (!wave_live) return;
@@ -415,7 +564,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnParams p) {
   if (my_row >= nrows) return;
   const bool empty = !(l_run > 0.f);
   const float inv_l = empty ? 0.f : 1.f / l_run;
-  const float lse_v = empty ? -INFINITY : (m_run + __builtin_amdgcn_logf(l_run)) * 0.69314718055994530942f;
+  const float lse_v = empty ? -INFINITY : (m_ref + __builtin_amdgcn_logf(l_run)) * 0.69314718055994530942f;
   const int64_t orow = q_row0 + my_row;
   if (PF || n_splits_i == 1) {
     uint16_t *o = static_cast<uint16_t *>(PF ? p.pf_out : p.out) + (orow * p.hq + h) * (int64_t)D;
@@ -423,8 +572,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(AttnParams p) {
     for (int db = 0; db < DB; ++db) {
       const int d = 16 * db + 4 * lg;
       uint2 v;
-      v.x = f32_to_bf16_bits(acc_o[db][0] * inv_l) | (f32_to_bf16_bits(acc_o[db][1] * inv_l) << 16);
-      v.y = f32_to_bf16_bits(acc_o[db][2] * inv_l) | (f32_to_bf16_bits(acc_o[db][3] * inv_l) << 16);
+      v.x = cvt_pk_bf16(acc_o[db][0] * inv_l, acc_o[db][1] * inv_l);
+      v.y = cvt_pk_bf16(acc_o[db][2] * inv_l, acc_o[db][3] * inv_l);
       *reinterpret_cast<uint2 *>(o + d) = v;
     }
     float *lse = PF ? p.pf_lse : p.lse;
@@ -656,8 +805,8 @@ struct Plan {
 };
 
 // Split plan of the verification set: KV rows per split (multiple of 64) and the number of
-// splits per request the grid provides.  Auto: aim for about two workgroups per CU (512)
-// when every request sits at max_ctx.
+// splits per request the grid provides.  Auto: aim for two workgroups per CU (512 on 256
+// CUs) when every request sits at max_ctx.
 static Plan make_plan(const dsv_attn_args *a) {
   Plan pl;
   if (a->n_bs <= 0 || a->dtype != DSV_BF16) return pl;
@@ -682,32 +831,47 @@ static Plan make_plan(const dsv_attn_args *a) {
   return pl;
 }
 
-template <int D, int NW>
-static void launch_verify(const AttnParams &p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((attn_bf16_kernel<D, NW, false>), dim3(grid), dim3(NW * 64),
-                     2 * kTileKV * D * sizeof(uint16_t), s, p);
+// Tile rows and ring depth per head_dim: 2-stage rings of 32 KB stages (16 KB for D = 64),
+// two workgroups per CU.
+template <int D> struct TileCfg;
+template <> struct TileCfg<64> { static constexpr int TILE = 64, VSTAGES = 4, PSTAGES = 4; };
+template <> struct TileCfg<128> { static constexpr int TILE = 64, VSTAGES = 2, PSTAGES = 2; };
+template <> struct TileCfg<256> { static constexpr int TILE = 32, VSTAGES = 2, PSTAGES = 2; };
+
+template <int D, int NW, bool PF>
+static bool launch_attn(const AttnParams &p, int grid, hipStream_t s) {
+  constexpr int TILE = TileCfg<D>::TILE;
+  constexpr bool DEEP = deep_schedule<D, NW>();
+  constexpr int NSTAGE = DEEP ? (PF ? TileCfg<D>::PSTAGES : TileCfg<D>::VSTAGES) : 2;
+  constexpr size_t shm = (size_t)NSTAGE * 2 * TILE * D * sizeof(uint16_t);
+  auto kern = attn_bf16_kernel<D, NW, PF, TILE, NSTAGE, DEEP>;
+  if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm) !=
+      hipSuccess)
+    return false;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), shm, s, p);
+  return true;
 }
 
 template <int D>
-static bool launch_verify_g(const AttnParams &p, int grid, hipStream_t s) {
+static int launch_verify_g(const AttnParams &p, int grid, hipStream_t s) {
   switch (p.G) {
-    case 1: launch_verify<D, 1>(p, grid, s); return true;
-    case 2: launch_verify<D, 2>(p, grid, s); return true;
-    case 3: launch_verify<D, 3>(p, grid, s); return true;
-    case 4: launch_verify<D, 4>(p, grid, s); return true;
-    case 5: launch_verify<D, 5>(p, grid, s); return true;
-    case 6: launch_verify<D, 6>(p, grid, s); return true;
-    case 7: launch_verify<D, 7>(p, grid, s); return true;
-    case 8: launch_verify<D, 8>(p, grid, s); return true;
-    case 9: launch_verify<D, 9>(p, grid, s); return true;
-    case 10: launch_verify<D, 10>(p, grid, s); return true;
-    case 11: launch_verify<D, 11>(p, grid, s); return true;
-    case 12: launch_verify<D, 12>(p, grid, s); return true;
-    case 13: launch_verify<D, 13>(p, grid, s); return true;
-    case 14: launch_verify<D, 14>(p, grid, s); return true;
-    case 15: launch_verify<D, 15>(p, grid, s); return true;
-    case 16: launch_verify<D, 16>(p, grid, s); return true;
-    default: return false;
+    case 1: return launch_attn<D, 1, false>(p, grid, s);
+    case 2: return launch_attn<D, 2, false>(p, grid, s);
+    case 3: return launch_attn<D, 3, false>(p, grid, s);
+    case 4: return launch_attn<D, 4, false>(p, grid, s);
+    case 5: return launch_attn<D, 5, false>(p, grid, s);
+    case 6: return launch_attn<D, 6, false>(p, grid, s);
+    case 7: return launch_attn<D, 7, false>(p, grid, s);
+    case 8: return launch_attn<D, 8, false>(p, grid, s);
+    case 9: return launch_attn<D, 9, false>(p, grid, s);
+    case 10: return launch_attn<D, 10, false>(p, grid, s);
+    case 11: return launch_attn<D, 11, false>(p, grid, s);
+    case 12: return launch_attn<D, 12, false>(p, grid, s);
+    case 13: return launch_attn<D, 13, false>(p, grid, s);
+    case 14: return launch_attn<D, 14, false>(p, grid, s);
+    case 15: return launch_attn<D, 15, false>(p, grid, s);
+    case 16: return launch_attn<D, 16, false>(p, grid, s);
+    default: return -1;
   }
 }
 
@@ -821,17 +985,11 @@ extern "C" dsv_status dsv_verify_attn(const dsv_attn_args *a, hipStream_t stream
       DSV_LAUNCH_CHECK();
     }
     if (a->dtype == DSV_BF16) {
-      const int64_t grid = (int64_t)p.pf_blocks * a->n_pf * a->hq;
-      const size_t shm = 2 * kTileKV * D * sizeof(uint16_t);
-      if (D == 64)
-        hipLaunchKernelGGL((attn_bf16_kernel<64, kPfWaves, true>), dim3((unsigned)grid),
-                           dim3(kPfWaves * 64), shm, stream, p);
-      else if (D == 128)
-        hipLaunchKernelGGL((attn_bf16_kernel<128, kPfWaves, true>), dim3((unsigned)grid),
-                           dim3(kPfWaves * 64), shm, stream, p);
-      else
-        hipLaunchKernelGGL((attn_bf16_kernel<256, kPfWaves, true>), dim3((unsigned)grid),
-                           dim3(kPfWaves * 64), shm, stream, p);
+      const int grid = (int)((int64_t)p.pf_blocks * a->n_pf * a->hq);
+      const bool ok = D == 64    ? launch_attn<64, kPfWaves, true>(p, grid, stream)
+                      : D == 128 ? launch_attn<128, kPfWaves, true>(p, grid, stream)
+                                 : launch_attn<256, kPfWaves, true>(p, grid, stream);
+      if (!ok) return DSV_ERR_HIP;
     } else {
       const int64_t grid = (int64_t)a->n_pf * a->pf_max_len * a->hq;
       if (D == 64)
@@ -848,10 +1006,11 @@ extern "C" dsv_status dsv_verify_attn(const dsv_attn_args *a, hipStream_t stream
     if (a->main_begin && hipEventRecord(a->main_begin, stream) != hipSuccess) return DSV_ERR_HIP;
     if (a->dtype == DSV_BF16) {
       const int64_t grid = (int64_t)pl.n_splits * a->n_bs * a->hkv;
-      bool ok = D == 64 ? launch_verify_g<64>(p, (int)grid, stream)
-                        : D == 128 ? launch_verify_g<128>(p, (int)grid, stream)
-                                   : launch_verify_g<256>(p, (int)grid, stream);
-      if (!ok) return DSV_ERR_UNSUPPORTED;
+      const int ok = D == 64    ? launch_verify_g<64>(p, (int)grid, stream)
+                     : D == 128 ? launch_verify_g<128>(p, (int)grid, stream)
+                                : launch_verify_g<256>(p, (int)grid, stream);
+      if (ok < 0) return DSV_ERR_UNSUPPORTED;
+      if (ok == 0) return DSV_ERR_HIP;
     } else {
       const int64_t grid = (int64_t)a->n_bs * a->W * a->hq;
       if (D == 64)
