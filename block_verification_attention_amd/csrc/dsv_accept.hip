@@ -72,14 +72,28 @@ __global__ __launch_bounds__(kAccThreads) void argmax_partial_kernel(
   bool nan = false;
   const int t = threadIdx.x;
   if (kVec4) {
-    for (int64_t v = lo + 4 * t; v < hi; v += 4 * kAccThreads) {
-      float4 f = *reinterpret_cast<const float4 *>(x + v);
-      float e[4] = {f.x, f.y, f.z, f.w};
+    // four independent 16-byte loads in flight per thread
+    constexpr int64_t kStep = 4 * kAccThreads;
+    for (int64_t v0 = lo + 4 * t; v0 < hi; v0 += 4 * kStep) {
+      float4 f[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        nan |= e[u] != e[u];
-        uint64_t key = ((uint64_t)ordered_bits(e[u]) << 32) | (uint32_t)~(uint32_t)(v + u);
-        best = key > best ? key : best;
+        const int64_t v = v0 + u * kStep;
+        const f32x4 ld = v < hi ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(x + v))
+                                : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        f[u] = make_float4(ld[0], ld[1], ld[2], ld[3]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t v = v0 + u * kStep;
+        if (v >= hi) continue;
+        const float e[4] = {f[u].x, f[u].y, f[u].z, f[u].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          nan |= e[q] != e[q];
+          uint64_t key = ((uint64_t)ordered_bits(e[q]) << 32) | (uint32_t)~(uint32_t)(v + q);
+          best = key > best ? key : best;
+        }
       }
     }
   } else {
@@ -116,12 +130,25 @@ __global__ __launch_bounds__(kAccThreads) void top2_partial_kernel(
   Top2 acc{0ull, 0u, 0u};
   const int t = threadIdx.x;
   if (kVec4) {
-    for (int64_t v = lo + 4 * t; v < hi; v += 4 * kAccThreads) {
-      float4 f = *reinterpret_cast<const float4 *>(x + v);
-      top2_push(acc, f.x, (uint32_t)v);
-      top2_push(acc, f.y, (uint32_t)v + 1);
-      top2_push(acc, f.z, (uint32_t)v + 2);
-      top2_push(acc, f.w, (uint32_t)v + 3);
+    constexpr int64_t kStep = 4 * kAccThreads;
+    for (int64_t v0 = lo + 4 * t; v0 < hi; v0 += 4 * kStep) {
+      float4 f[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t v = v0 + u * kStep;
+        const f32x4 ld = v < hi ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(x + v))
+                                : f32x4{0.f, 0.f, 0.f, 0.f};
+        f[u] = make_float4(ld[0], ld[1], ld[2], ld[3]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t v = v0 + u * kStep;
+        if (v >= hi) continue;
+        top2_push(acc, f[u].x, (uint32_t)v);
+        top2_push(acc, f[u].y, (uint32_t)v + 1);
+        top2_push(acc, f[u].z, (uint32_t)v + 2);
+        top2_push(acc, f[u].w, (uint32_t)v + 3);
+      }
     }
   } else {
     for (int64_t v = lo + t; v < hi; v += kAccThreads) top2_push(acc, x[v], (uint32_t)v);
@@ -145,14 +172,22 @@ __global__ __launch_bounds__(kAccThreads) void top2_partial_kernel(
   }
 }
 
-// Target choice of slot s from its chunk keys (-1 for a NaN row).
-__device__ __forceinline__ int32_t argmax_from_keys(const uint64_t *keys, int64_t s, int n_chunks) {
-  uint64_t r = 0;
-  for (int c = 0; c < n_chunks; ++c) {
-    uint64_t v = keys[s * n_chunks + c];
-    r = v > r ? v : r;
-  }
+__device__ __forceinline__ int32_t key_to_index(uint64_t r) {
   return r == kNanKey ? -1 : (int32_t)(~(uint32_t)r);
+}
+
+// Largest chunk key of slot s, considering chunks c0, c0 + step, ... (four loads in flight).
+__device__ __forceinline__ uint64_t max_chunk_key(const uint64_t *keys, int64_t s, int n_chunks,
+                                                  int c0, int step) {
+  uint64_t r = 0;
+  for (int c = c0; c < n_chunks; c += 4 * step) {
+    uint64_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = c + u * step < n_chunks ? keys[s * n_chunks + c + u * step] : 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) r = v[u] > r ? v[u] : r;
+  }
+  return r;
 }
 
 // One wavefront per request.
@@ -171,7 +206,7 @@ __global__ __launch_bounds__(kWave) void accept_finalize_kernel(
     end = end < 0 ? 0 : (end > m_bs ? m_bs : end);
     // every slot's choice: grid-stride over all m_bs slots
     for (int64_t s = (int64_t)i * kWave + lane; s < m_bs; s += (int64_t)n_bs * kWave)
-      slot_argmax[s] = s < end ? argmax_from_keys(keys, s, n_chunks) : -1;
+      slot_argmax[s] = s < end ? key_to_index(max_chunk_key(keys, s, n_chunks, 0, 1)) : -1;
 
     const int ki = k[i], off = offsets[i];
     const bool ok = ki >= 0 && ki <= W && off >= 0 && (int64_t)off + ki <= end;
@@ -191,8 +226,16 @@ __global__ __launch_bounds__(kWave) void accept_finalize_kernel(
       }
       if (out_tokens && lane < W) out_tokens[(int64_t)i * W + lane] = -1;
     } else {
+      // four lanes per row (16 rows per wavefront) reduce the row's chunk keys
+      const int jr = lane >> 2, q = lane & 3;
+      uint64_t kr = jr < ki ? max_chunk_key(keys, off + jr, n_chunks, q, 4) : 0;
+      uint64_t o1 = shfl_xor_u64(kr, 1);
+      kr = o1 > kr ? o1 : kr;
+      o1 = shfl_xor_u64(kr, 2);
+      kr = o1 > kr ? o1 : kr;
       // lane j holds the target's choice at slot off + j and the draft token there
-      const int32_t g = lane < ki ? argmax_from_keys(keys, off + lane, n_chunks) : -1;
+      const uint64_t kj = shfl_u64(kr, 4 * (lane & 15));
+      const int32_t g = lane < ki ? key_to_index(kj) : -1;
       const int32_t tok = lane < ki ? slot_tok[off + lane] : -1;
       const int32_t g_prev = __shfl(g, lane > 0 ? lane - 1 : 0);
       const bool mismatch = lane >= 1 && lane < ki && tok != g_prev;

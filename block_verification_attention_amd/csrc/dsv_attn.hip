@@ -260,6 +260,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
 
   // ---- work unit ----
   int g, h, c, r_lo, r_hi, row0, nrows, split = 0, n_splits_i = 1, off = 0;
+  bool stored = false;  // this workgroup wrote global memory before the tile loop
   int64_t kb, q_row0;
   const uint16_t *qsrc;
   const uint16_t *knew = nullptr, *vnew = nullptr;
@@ -271,6 +272,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     split = t / p.n_bs;
     h = g * p.G + w;
     if (i == 0 && split == 0) {
+      stored = true;
       int end = p.offsets[p.n_bs];
       end = end < 0 ? 0 : (end > p.m_bs ? p.m_bs : end);
       zero_rows_bf16<D>(static_cast<uint16_t *>(p.out), p.lse, p.hq, end, p.m_bs, g * p.G, p.G,
@@ -301,6 +303,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
       vnew = static_cast<const uint16_t *>(p.v_new);
       // this step's KV writes: the candidates this split covers go to their cache references
       const int p0 = max(c, r_lo), p1 = r_hi;
+      stored = stored || p1 > p0;
       constexpr int C16 = D / 8;
       for (int e = tid; e < (p1 - p0) * C16 * 2; e += NW * 64) {
         const int isv = e / ((p1 - p0) * C16);
@@ -353,8 +356,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     }
   }
   const int lim = c + my_row;  // last visible position of this lane's query row
-  // every plain global access above is complete before the LDS loads start
-  __builtin_amdgcn_s_waitcnt(0);
+  // The LDS loads' completion is counted against this wave's vector-memory counter, which
+  // loads and stores share: stores issued above must be complete first.  (Loads issued above,
+  // such as the query fragment, complete before the younger LDS loads.)
+  if (stored) __builtin_amdgcn_s_waitcnt(0);
 
   // ---- tile loads: wave w issues loads q = w, w + NW, ... of the 2 * NCK per tile ----
   const int64_t row_elems = p.stride_row;
@@ -593,7 +598,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
 
 // ---------------------------------------------------------------------------
 // Split-KV merge: out = sum_s e^{lse_s - M} o_s / sum_s e^{lse_s - M}, lse = M + ln(sum),
-// splits taken in increasing order (deterministic).  Half a wavefront (32 lanes x 4 floats)
+// splits taken in increasing order with a running maximum (deterministic).  Half a wavefront (32 lanes x 4 floats)
 // per (slot, query head) row of D = 128 (D/4 lanes in general), all of a row's split loads
 // issued before they are consumed.  Requests whose KV range fits one split were written
 // directly by the main kernel.
@@ -615,22 +620,24 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   if (S <= 1) return;
   const int64_t plane = (int64_t)p.m_bs * p.hq;
   const int64_t rh = (int64_t)(off + j) * p.hq + h;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, p.ws_lse[s * plane + rh]);
-  float den = 0.f;
+  // one pass with a running maximum; the loads of up to eight splits are issued together
+  float M = -INFINITY, den = 0.f;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
   const float4 *src = reinterpret_cast<const float4 *>(p.ws_o + rh * D) + l4;
   const int64_t step4 = plane * D / 4;
 #pragma unroll 8
   for (int s = 0; s < S; ++s) {
     const float ls = p.ws_lse[s * plane + rh];
-    const float wgt = ls == -INFINITY ? 0.f : __expf(ls - M);
     const float4 o = src[s * step4];
-    den += wgt;
-    num.x += wgt * o.x;
-    num.y += wgt * o.y;
-    num.z += wgt * o.z;
-    num.w += wgt * o.w;
+    const float m_new = fmaxf(M, ls);
+    const float a = m_new == -INFINITY ? 1.f : __expf(M - m_new);   // rescale of the sum so far
+    const float b = ls == -INFINITY ? 0.f : __expf(ls - m_new);     // weight of split s
+    den = den * a + b;
+    num.x = num.x * a + b * o.x;
+    num.y = num.y * a + b * o.y;
+    num.z = num.z * a + b * o.z;
+    num.w = num.w * a + b * o.w;
+    M = m_new;
   }
   const float inv = 1.f / den;
   uint2 v;

@@ -165,3 +165,28 @@ def test_max_ctx_plan_exceeded_is_flagged():
     assert int(d["status"].item()) & dsv.STATUS_POOL
     assert torch.all(out[0:4] == 0)
     assert torch.isfinite(out[4:8].float()).all()
+
+
+def test_workspace_reused_across_calls():
+    """One workspace serves consecutive calls at a fixed address, across different requests."""
+    cases = [small_case(47 + s, hq=8, hkv=2, d=128, k=(16, 7, 3), ctx=(900, 1500, 64)) for s in range(3)]
+    dev_ws = None
+    for c in cases:
+        d = device_case(c)
+        packed = gpu_pack(c, d)
+        out = torch.full_like(d["q"], float("nan"))
+        lse = torch.full((c["m_bs"], c["hq"]), float("nan"), device=DEV)
+        args = dsv.attn_args(d["q"], d["k_pool"], d["v_pool"], packed["offsets"], d["k"], d["ctx_len"],
+                             d["kv_base"], W=16, max_ctx=1500, out=out, status=d["status"], lse=lse,
+                             k_new=d["k_new"], v_new=d["v_new"], slot_cache_loc=packed["slot_cache_loc"],
+                             kv_chunk=128)
+        need = dsv.verify_attn_workspace_bytes(args)
+        if dev_ws is None:
+            dev_ws = torch.full((need,), 0xAB, dtype=torch.uint8, device=DEV)  # no clearing needed
+        args.workspace, args.workspace_bytes = dev_ws.data_ptr(), dev_ws.numel()
+        dsv.verify_attn_call(args)
+        torch.cuda.synchronize()
+        assert int(d["status"].item()) == 0
+        ref = oracle_pack(c)
+        r_o, r_l = oracle_attn(c, ref["offsets"])
+        compare_attn(c, ref["offsets"], out, lse, r_o, r_l, tag=f"reuse {c['name']}")
