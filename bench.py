@@ -10,10 +10,16 @@ Inputs are resident in HBM before timing.  To keep the 256 MiB Infinity Cache fr
 the KV stream, the step rotates over enough copies of the KV pool and logits to exceed 1 GB
 (each copy holds the same seeded values).
 
-Prints one JSON line.  `value` is verified slots per second of the whole step; `roofline`
-reports the verification-attention kernel (the dominant one): algorithmic KV bytes per
-launch (every visible K and V row read once) over its average duration measured with HIP
-events on the launch stream.  `cpu_baseline` times the CPU oracle on a bounded sample.
+Two timed passes over the same steps: (1) direct calls, with HIP events recorded by the
+library around every verification-attention kernel on its launch stream; (2) the same steps
+captured once each as HIP graphs and replayed (the library's calls allocate nothing, never
+synchronise the host and record no memset, so a serving loop can replay them).
+
+Prints one JSON line.  `value` is verified slots per second of the whole step (graph replay;
+`--no-graph` reports the direct-call pass); `roofline` reports the verification-attention
+kernel (the dominant one): algorithmic KV bytes per launch (every visible K and V row read
+once) over its average duration from pass (1), against 8 TB/s and against the box's measured
+streaming-read ceiling.  `cpu_baseline` times the CPU oracle on a bounded sample.
 """
 from __future__ import annotations
 
@@ -100,6 +106,8 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="KV/logits copies rotated per step")
     ap.add_argument("--kv-chunk", type=int, default=0)
     ap.add_argument("--cpu-sample", type=int, default=8, help="requests in the oracle sample (0 = skip)")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="launch each step's calls directly instead of replaying a captured HIP graph")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a "
@@ -141,39 +149,58 @@ def main():
     ev = HipEvents()
     n_total = args.warmup + args.steps
     main_ev = ev.create(2 * n_total)
-    attn_args = []
-    for s in range(n_total):
+    max_ctx = int(c["ctx_len"].max())
+
+    def make_args(s, events):
         kp, vp, _ = pools[s % len(pools)]
-        a = dsv.attn_args(q, kp, vp, packed["offsets"], k, ctx, base, W=W,
-                          max_ctx=int(c["ctx_len"].max()), out=out, status=status, lse=lse,
-                          k_new=k_new, v_new=v_new, slot_cache_loc=packed["slot_cache_loc"],
-                          kv_chunk=args.kv_chunk, events=(main_ev[2 * s].value, main_ev[2 * s + 1].value))
-        attn_args.append(a)
-    ws_bytes = dsv.verify_attn_workspace_bytes(attn_args[0])
+        return dsv.attn_args(q, kp, vp, packed["offsets"], k, ctx, base, W=W, max_ctx=max_ctx,
+                             out=out, status=status, lse=lse, k_new=k_new, v_new=v_new,
+                             slot_cache_loc=packed["slot_cache_loc"], kv_chunk=args.kv_chunk,
+                             events=events)
+
+    timed_args = [make_args(s, (main_ev[2 * s].value, main_ev[2 * s + 1].value)) for s in range(n_total)]
+    plain_args = [make_args(s, None) for s in range(n_total)]
+    ws_bytes = dsv.verify_attn_workspace_bytes(timed_args[0])
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
-    for a in attn_args:
+    for a in timed_args + plain_args:
         a.workspace = ws.data_ptr()
         a.workspace_bytes = ws.numel()
     acc_ws = torch.empty(max(dsv.accept_workspace_bytes(m_bs, c["logits"].shape[1], 0, 0, 0), 256),
                          dtype=torch.uint8, device=dev)
 
-    def step(s):
+    def step(s, arg_list):
         dsv.pack_slots(k, ctx, base, tok, m_bs, status, out=packed)
-        dsv.verify_attn_call(attn_args[s])
+        dsv.verify_attn_call(arg_list[s])
         dsv.accept(n_bs=c["n_bs"], W=W, status=status, target_logits=pools[s % len(pools)][2],
                    slot_tok=packed["slot_tok"], offsets=packed["offsets"], k=k, out=acc_out,
                    workspace=acc_ws)
 
+    def timed(fn):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1)
+
     for s in range(args.warmup):
-        step(s)
-    torch.cuda.synchronize()
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_start.record()
-    for s in range(args.warmup, n_total):
-        step(s)
-    t_end.record()
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
+        step(s, plain_args)
+    # timed region 1: direct calls, HIP events around every verification-attention kernel
+    direct_ms = timed(lambda: [step(s, timed_args) for s in range(args.warmup, n_total)])
+    total_ms = direct_ms
+    if args.graph:
+        # one captured step per timed step (each with its own KV copy); the library makes no
+        # allocation, host synchronisation or memset inside its calls
+        graphs = []
+        for s in range(args.warmup, n_total):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(s, plain_args)
+            graphs.append(g)
+        graphs[0].replay()
+        # timed region 2: the same steps replayed as HIP graphs
+        total_ms = timed(lambda: [g.replay() for g in graphs])
     st = int(status.item())
     if st != 0:
         print(json.dumps({"error": f"device status {st}"}))
@@ -209,6 +236,7 @@ def main():
             "n_requests": 8, "slots": slots, "context": 8192, "hq": 32, "hkv": 8, "head_dim": 128,
             "vocab": 151936, "step": "pack + verify attention (incl. candidate KV write, split-KV "
                                       "merge) + accept",
+            "launch": "HIP graph per step" if args.graph else "direct calls",
         },
         "roofline": {
             "kernel": PROFILED_KERNEL,
@@ -222,7 +250,28 @@ def main():
             "avg_launch_us": attn_avg_ms * 1e3,
         },
         "attn_kernel_slots_per_s": slots / (attn_avg_ms * 1e-3),
+        "direct_call_ms_per_step": direct_ms / args.steps,
     }
+    # practical read ceiling of this machine: a plain streaming read of the same KV bytes
+    lib = dsv._lib.load()
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    probe_ms = []
+    for s in range(3 + args.steps):
+        kp, vp, _ = pools[s % len(pools)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for t in (kp, vp):
+            dsv._lib.check(lib.dsv_probe_stream_read(ctypes.c_void_p(t.data_ptr()), t.numel() * 2,
+                                                     ctypes.c_void_p(sink.data_ptr()), stream),
+                           "dsv_probe_stream_read")
+        e1.record()
+        probe_ms.append((e0, e1))
+    torch.cuda.synchronize()
+    probe_avg = float(np.mean([a.elapsed_time(b) for a, b in probe_ms[3:]]))
+    pool_bytes = 2 * kp0.numel() * 2
+    res["roofline"]["stream_read_ceiling_GBs"] = pool_bytes / (probe_avg * 1e-3) / 1e9
+    res["roofline"]["frac_of_ceiling"] = achieved / res["roofline"]["stream_read_ceiling_GBs"]
     if args.cpu_sample > 0:
         res["cpu_baseline"] = cpu_baseline(c, args.cpu_sample)
     print(json.dumps(res))

@@ -852,9 +852,14 @@ static bool launch_attn(const AttnParams &p, int grid, hipStream_t s) {
   constexpr int NSTAGE = DEEP ? (PF ? TileCfg<D>::PSTAGES : TileCfg<D>::VSTAGES) : 2;
   constexpr size_t shm = (size_t)NSTAGE * 2 * TILE * D * sizeof(uint16_t);
   auto kern = attn_bf16_kernel<D, NW, PF, TILE, NSTAGE, DEEP>;
-  if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm) !=
-      hipSuccess)
-    return false;
+  // once per kernel (idempotent), so that a captured call contains launches only
+  static bool lds_limit_set = false;
+  if (!lds_limit_set) {
+    if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm) !=
+        hipSuccess)
+      return false;
+    lds_limit_set = true;
+  }
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), shm, s, p);
   return true;
 }

@@ -243,6 +243,17 @@ dsv_status dsv_accept(int32_t n_bs, int32_t m_bs, int32_t W, int32_t vocab,
                       void *workspace, size_t workspace_bytes, int32_t *status,
                       hipStream_t stream);
 
+/* ------------------------------------------------------------------------ */
+/* dsv_probe_stream_read -- measurement helper (not part of the method)      */
+/*                                                                            */
+/* Reads `bytes` (rounded down to 16) of device memory at `buf` (16-byte     */
+/* aligned) with plain streaming loads, so that a caller can time the        */
+/* practical HBM read ceiling that the verification kernel's bandwidth is    */
+/* compared with.  `sink` is a device float that is written only in a        */
+/* pathological case (it keeps the loads alive).  Enqueued on `stream`.      */
+/* ------------------------------------------------------------------------ */
+dsv_status dsv_probe_stream_read(const void *buf, size_t bytes, float *sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

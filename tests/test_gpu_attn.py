@@ -190,3 +190,51 @@ def test_workspace_reused_across_calls():
         ref = oracle_pack(c)
         r_o, r_l = oracle_attn(c, ref["offsets"])
         compare_attn(c, ref["offsets"], out, lse, r_o, r_l, tag=f"reuse {c['name']}")
+
+
+def test_step_graph_capture_replays_match_eager():
+    """The three calls of a step (pack, verify attention with candidate KV writes and split
+    merge, accept) are capturable: a captured step replayed several times, with eager work and
+    synchronisation between replays, reproduces the eager outputs bit for bit each time."""
+    c = small_case(48, hq=8, hkv=2, d=128, k=(16, 9, 1, 12), ctx=(700, 1300, 5, 260), vocab=3000)
+    d = device_case(c)
+    logits = to_dev(c["logits"])
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device=DEV)
+    acc_ws = torch.zeros(1 << 20, dtype=torch.uint8, device=DEV)
+    packed = dsv.pack_slots(d["k"], d["ctx_len"], d["kv_base"], d["block_tokens"], c["m_bs"], d["status"])
+    out = torch.zeros_like(d["q"])
+    lse = torch.zeros((c["m_bs"], c["hq"]), device=DEV)
+    acc = {}
+
+    def step():
+        dsv.pack_slots(d["k"], d["ctx_len"], d["kv_base"], d["block_tokens"], c["m_bs"], d["status"], out=packed)
+        a = dsv.attn_args(d["q"], d["k_pool"], d["v_pool"], packed["offsets"], d["k"], d["ctx_len"],
+                          d["kv_base"], W=16, max_ctx=1300, out=out, status=d["status"], lse=lse,
+                          k_new=d["k_new"], v_new=d["v_new"], slot_cache_loc=packed["slot_cache_loc"],
+                          kv_chunk=256, workspace=ws)
+        dsv.verify_attn_call(a)
+        dsv.accept(n_bs=c["n_bs"], W=16, status=d["status"], target_logits=logits,
+                   slot_tok=packed["slot_tok"], offsets=packed["offsets"], k=d["k"], out=acc, workspace=acc_ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = (out.clone(), lse.clone(), {key: v.clone() for key, v in acc.items()})
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(3):
+        out.zero_()
+        lse.zero_()
+        for v in acc.values():
+            v.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager[0].view(torch.int16)), f"replay {r}"
+        assert torch.equal(lse, eager[1]), f"replay {r}"
+        for key, v in acc.items():
+            assert torch.equal(v, eager[2][key]), f"replay {r} {key}"
+    assert int(d["status"].item()) == 0
+    ref = oracle_pack(c)
+    r_o, r_l = oracle_attn(c, ref["offsets"])
+    compare_attn(c, ref["offsets"], out, lse, r_o, r_l, tag="graph")
