@@ -37,30 +37,26 @@ def hipcc() -> str:
     return "hipcc"
 
 
-# attn_bf16_kernel<D, NW, PF, TILE, NSTAGE, DEEP>
-_ATTN_KERNEL = re.compile(r"attn_bf16_kernelILi(\d+)ELi(\d+)ELb([01])ELi(\d+)ELi(\d+)ELb([01])E")
+# attn_bf16_kernel<D, NW, PF, TILE>
+_ATTN_KERNEL = re.compile(r"attn_bf16_kernelILi(\d+)ELi(\d+)ELb([01])ELi(\d+)E")
 
 
-def check_deep_kernels_without_scratch(remarks: str) -> int:
-    """The multi-stage schedule of the attention kernel counts its own outstanding loads;
-    a register spill (scratch access) inside that window would break the count.  Every
-    instantiation compiled with that schedule must therefore use no scratch.  Returns the
-    number of such kernels checked; raises if one uses scratch."""
-    checked = 0
-    current = None
+def attn_kernel_resources(remarks: str) -> dict:
+    """Per attention-kernel instantiation (D, waves, prefill): VGPRs, AGPRs, scratch bytes per
+    lane and occupancy (waves per SIMD), parsed from the compiler's resource-usage remarks."""
+    res, cur = {}, None
     for line in remarks.splitlines():
         if "Function Name:" in line:
             m = _ATTN_KERNEL.search(line)
-            current = m if (m and m.group(6) == "1") else None
-        elif current is not None and "ScratchSize [bytes/lane]:" in line:
-            size = int(line.rsplit(":", 1)[1].split()[0])
-            if size != 0:
-                d, nw = current.group(1), current.group(2)
-                raise RuntimeError(f"attention kernel D={d} waves={nw} (multi-stage schedule) uses "
-                                   f"{size} B/lane of scratch; move it to the conservative schedule")
-            checked += 1
-            current = None
-    return checked
+            cur = (int(m.group(1)), int(m.group(2)), m.group(3) == "1") if m else None
+            if cur:
+                res[cur] = {}
+        elif cur is not None:
+            for key, name in (("VGPRs:", "vgpr"), ("AGPRs:", "agpr"), ("ScratchSize [bytes/lane]:", "scratch"),
+                              ("Occupancy [waves/SIMD]:", "occupancy")):
+                if key in line:
+                    res[cur][name] = int(line.rsplit(":", 1)[1].split()[0])
+    return res
 
 
 def build(verbose: bool = False) -> str:
@@ -85,9 +81,12 @@ def build(verbose: bool = False) -> str:
         if proc.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n" + "\n".join(lines))
         if src == "dsv_attn.hip":
-            n = check_deep_kernels_without_scratch("\n".join(lines))
-            if n == 0:
-                raise RuntimeError("no multi-stage attention kernel found in the resource report")
+            res = attn_kernel_resources("\n".join(lines))
+            if not res:
+                raise RuntimeError("no attention kernel found in the resource report")
+            if verbose:
+                for (d, nw, pf), r in sorted(res.items()):
+                    print(f"attn_bf16_kernel D={d} waves={nw} prefill={pf}: {r}")
             lines = [l for l in lines if "remark:" not in l and "kernel-resource-usage" not in l]
         msg = "\n".join(lines)
         if msg.strip() and verbose:

@@ -40,6 +40,9 @@
 namespace dsv {
 
 constexpr int kTileKV = 64;  // split granularity (multiple of every tile height)
+// Waves with at most this many 16-byte loads per tile stage two tiles in registers (more
+// would push the hot shapes past the register budget of two waves per SIMD).
+constexpr int kTwoSetMaxLoads = 4;
 constexpr int kPfWaves = 8;  // 8 waves x 16 rows = 128-row prefill tile
 constexpr int kPfRows = kPfWaves * 16;
 
@@ -77,9 +80,18 @@ __device__ __forceinline__ int verify_request(const AttnParams &p, int i, int &k
   kb = p.kv_base[i];
   if (ki < 0 || ki > p.W || off < 0 || (int64_t)off + ki > p.m_bs || c < 0 || kb < 0)
     return DSV_STATUS_BAD_REQUEST;
-  if (kb + c + ki > p.pool_rows || (int64_t)c + ki > (int64_t)p.n_splits * p.chunk)
-    return DSV_STATUS_POOL;
+  if (kb + c + ki > p.pool_rows) return DSV_STATUS_POOL;
   return 0;
+}
+
+// Splits of a verification request with n_vis visible positions: floor(n_vis / chunk) of them
+// (at least one, at most the planned count); split s covers [s * chunk, (s + 1) * chunk) and
+// the last one also takes the remainder, so every split has at least `chunk` rows and at most
+// the last is longer.
+__device__ __forceinline__ int verify_splits(const AttnParams &p, int n_vis) {
+  int s = n_vis / p.chunk;
+  s = s < 1 ? 1 : s;
+  return s > p.n_splits ? p.n_splits : s;
 }
 
 __device__ __forceinline__ int prefill_request(const AttnParams &p, int r, int &ql, int &qs, int &c,
@@ -113,74 +125,18 @@ __device__ void zero_rows_bf16(uint16_t *out, float *lse, int hq, int r0, int r1
 }
 
 // ---------------------------------------------------------------------------
-// Direct global->LDS loads.  Each lane of a wave moves 16 bytes; the wave's 64 x 16 B land
-// contiguously at the wave-uniform LDS address in m0, so the XOR swizzle of the tile is
-// applied on the global side (each lane picks which 16-byte column slot of its row it
-// fetches).  Completion is tracked with vmcnt, waited for explicitly: the compiler would
-// otherwise wait for every outstanding LDS load before each barrier, which collapses the
-// multi-stage ring to a single stage.
-// Interior tiles use a buffer descriptor over the request's KV segment with a lane-constant
-// VGPR offset and a per-tile scalar offset (no per-tile vector address arithmetic);
-// boundary tiles (candidate rows from k_new, rows past the range) use per-lane addresses.
+// KV staging.  Each wave loads its share of a tile from HBM into registers (16 bytes per lane,
+// consecutive lanes on consecutive bytes of a row, non-temporal: the KV is streamed once) and
+// later stores it to an LDS stage with the XOR swizzle applied on the LDS side.  Two register
+// sets and two LDS stages keep two tiles in flight while a third is consumed; the compiler
+// tracks completion of the register loads.  (Direct global->LDS loads, measured on the same
+// access pattern, sustained about 12% less bandwidth than loads through registers.)
 // ---------------------------------------------------------------------------
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ void lds_dma16(uint32_t lds_wave_base, const void *src) {
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(lds_wave_base), "v"(src)
-               : "memory", "m0");
-#pragma clang diagnostic pop
-}
-
-__device__ __forceinline__ void lds_dma16_buf(uint32_t lds_wave_base, i32x4 rsrc_in, uint32_t voff,
-                                              uint32_t soff) {
-  i32x4 rsrc;  // the descriptor must live in scalar registers
-  rsrc[0] = __builtin_amdgcn_readfirstlane(rsrc_in[0]);
-  rsrc[1] = __builtin_amdgcn_readfirstlane(rsrc_in[1]);
-  rsrc[2] = __builtin_amdgcn_readfirstlane(rsrc_in[2]);
-  rsrc[3] = __builtin_amdgcn_readfirstlane(rsrc_in[3]);
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(lds_wave_base), "v"(voff), "s"(rsrc), "s"(soff)
-               : "memory", "m0");
-#pragma clang diagnostic pop
-}
-
-// Raw buffer descriptor (stride 0, 32-bit byte offsets) over [base, base + bytes).
-__device__ __forceinline__ i32x4 buffer_rsrc(const void *base, uint32_t bytes) {
-  const uint64_t a = (uint64_t)(uintptr_t)base;
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
-  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
-  r[3] = 0x00020000;
-  return r;
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Waits until this wave's loads of every tile issued before the last `after` tiles are
-// complete (per tile each wave issues at least PER loads).  vmcnt holds at most 63; a larger
-// count is clamped, which only waits a little longer than needed.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_clamped() {
-  wait_vmcnt<(N > 63 ? 63 : N)>();
-}
-template <int PER, int NSTAGE>
-__device__ __forceinline__ void wait_tiles(int after) {
-  if (NSTAGE > 3 && after >= 3) wait_vmcnt_clamped<PER * 3>();
-  else if (NSTAGE > 2 && after >= 2) wait_vmcnt_clamped<PER * 2>();
-  else if (NSTAGE > 1 && after >= 1) wait_vmcnt_clamped<PER>();
-  else wait_vmcnt<0>();
-}
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+struct Piece {  // 16 staged bytes
+  uint32_t a, b, c, d;
+};
 
 // LDS tile layouts: row-major [TILE][D] bf16 for both K and V, 16-byte column slots permuted
 // per row.  K: slot ^ (row & 15) -- the 16 rows of an MFMA operand read (one slot each) land
@@ -219,37 +175,24 @@ constexpr float kRescaleSlack = 8.0f;
 // tile per query head, split KV).  PF = true: prefill (NW = 8 waves along the query rows of
 // one head).  KV tiles of TILE rows stream through an NSTAGE-deep LDS ring.
 // ---------------------------------------------------------------------------
-// Schedules.  DEEP: NSTAGE - 1 tiles in flight while one is consumed; the wait counts this
-// wave's own loads exactly, which is only valid when no other vector-memory instruction (such
-// as a register spill) can sit between the loads and the wait -- the build checks that every
-// DEEP instantiation uses no scratch.  Otherwise: wait for everything, then issue the next
-// tile and compute the current one (one tile in flight during the computation).
-// DEEP is limited to workgroups of 3..8 waves with head_dim <= 128 (2..16 waves for 64): those
-// keep at most 32 of their own loads in flight per wave and fit the register file without
-// spilling into accumulation registers.  Single- and two-wave workgroups with 128-wide rows
-// and every head_dim-256 shape use the conservative schedule.
-template <int D, int NW>
-constexpr bool deep_schedule() {
-  return (D == 64 && NW >= 2) || (D == 128 && NW >= 3 && NW <= 8);
-}
 template <int D, int NW>
 constexpr int waves_per_eu_hint() {
   // small workgroups get the whole register file; 3..8 waves are asked to fit 2 waves/SIMD
   return (NW <= 2 || (D == 256 && NW <= 4)) ? 1 : (NW <= 8 ? 2 : 1);
 }
 
-template <int D, int NW, bool PF, int TILE, int NSTAGE, bool DEEP>
+template <int D, int NW, bool PF, int TILE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_per_eu_hint<D, NW>()))) void attn_bf16_kernel(AttnParams p) {
   constexpr int RPC = 1024 / (2 * D);        // rows per 1 KB wave load
   constexpr int NCK = TILE / RPC;            // wave loads per tensor per tile
-  constexpr int PER = (2 * NCK) / NW;        // wave loads per wave per tile (at least)
   constexpr int QPW = (2 * NCK + NW - 1) / NW;  // wave loads per wave per tile (at most)
+  constexpr int RSETS = QPW <= kTwoSetMaxLoads ? 2 : 1;  // register sets (tiles in flight besides LDS)
   constexpr int STAGE_BYTES = 2 * TILE * D * 2;
   constexpr int DB = D / 16;
   constexpr int KS = D / 32;
   constexpr int KB = TILE / 16;              // 16-row score blocks per tile
   constexpr int KK = TILE / 32;              // 32-row P.V steps per tile
-  static_assert(TILE % 32 == 0 && TILE % RPC == 0 && PER >= 1, "tile shape");
+  static_assert(TILE % 32 == 0 && TILE % RPC == 0, "tile shape");
 
   extern __shared__ __align__(16) uint16_t lds[];
   const uint32_t lds_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)lds;
@@ -260,7 +203,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
 
   // ---- work unit ----
   int g, h, c, r_lo, r_hi, row0, nrows, split = 0, n_splits_i = 1, off = 0;
-  bool stored = false;  // this workgroup wrote global memory before the tile loop
   int64_t kb, q_row0;
   const uint16_t *qsrc;
   const uint16_t *knew = nullptr, *vnew = nullptr;
@@ -272,7 +214,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     split = t / p.n_bs;
     h = g * p.G + w;
     if (i == 0 && split == 0) {
-      stored = true;
       int end = p.offsets[p.n_bs];
       end = end < 0 ? 0 : (end > p.m_bs ? p.m_bs : end);
       zero_rows_bf16<D>(static_cast<uint16_t *>(p.out), p.lse, p.hq, end, p.m_bs, g * p.G, p.G,
@@ -290,10 +231,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
       return;
     }
     const int n_vis = c + ki;
-    n_splits_i = (n_vis + p.chunk - 1) / p.chunk;
+    n_splits_i = verify_splits(p, n_vis);
     if (ki == 0 || split >= n_splits_i) return;
     r_lo = split * p.chunk;
-    r_hi = min(n_vis, r_lo + p.chunk);
+    r_hi = split == n_splits_i - 1 ? n_vis : r_lo + p.chunk;
     row0 = 0;
     nrows = ki;
     q_row0 = off;
@@ -301,24 +242,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     if (p.k_new) {
       knew = static_cast<const uint16_t *>(p.k_new);
       vnew = static_cast<const uint16_t *>(p.v_new);
-      // this step's KV writes: the candidates this split covers go to their cache references
-      const int p0 = max(c, r_lo), p1 = r_hi;
-      stored = stored || p1 > p0;
-      constexpr int C16 = D / 8;
-      for (int e = tid; e < (p1 - p0) * C16 * 2; e += NW * 64) {
-        const int isv = e / ((p1 - p0) * C16);
-        const int rem = e % ((p1 - p0) * C16);
-        const int pos = p0 + rem / C16, cc = rem % C16;
-        const int64_t loc = p.slot_cache_loc[off + pos - c];
-        if (loc < 0 || loc >= p.pool_rows) {
-          status_or(p.status, DSV_STATUS_POOL);
-          continue;
-        }
-        const uint16_t *src = (isv ? vnew : knew) + ((int64_t)(off + pos - c) * p.hkv + g) * D + cc * 8;
-        uint16_t *dst = static_cast<uint16_t *>(isv ? p.v_pool : p.k_pool) + g * p.stride_head +
-                        loc * p.stride_row + cc * 8;
-        *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
-      }
     }
   } else {
     const int bid = blockIdx.x;
@@ -356,21 +279,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     }
   }
   const int lim = c + my_row;  // last visible position of this lane's query row
-  // The LDS loads' completion is counted against this wave's vector-memory counter, which
-  // loads and stores share: stores issued above must be complete first.  (Loads issued above,
-  // such as the query fragment, complete before the younger LDS loads.)
-  if (stored) __builtin_amdgcn_s_waitcnt(0);
 
-  // ---- tile loads: wave w issues loads q = w, w + NW, ... of the 2 * NCK per tile ----
+  // ---- tile loads: wave w moves pieces q = w, w + NW, ... of the 2 * NCK per tile (piece q
+  // < NCK: K rows RPC q .. + RPC - 1, else the same rows of V; 16 bytes per lane) ----
   const int64_t row_elems = p.stride_row;
   const uint32_t row_bytes = (uint32_t)(row_elems * 2);
   const uint16_t *kseg = static_cast<const uint16_t *>(p.k_pool) + g * p.stride_head + kb * row_elems;
   const uint16_t *vseg = static_cast<const uint16_t *>(p.v_pool) + g * p.stride_head + kb * row_elems;
   // rows [0, n_fast) of the request come from the pool; interior tiles lie below it
   const int n_fast = knew ? min(r_hi, c) : r_hi;
-  const i32x4 krsrc = buffer_rsrc(kseg, 0xffffffffu);
-  const i32x4 vrsrc = buffer_rsrc(vseg, 0xffffffffu);
-  uint32_t voff[QPW];
+  // With NCK a multiple of NW every wave moves the same pieces pattern: its first NCK / NW
+  // pieces are K, the rest V, and none is past the tile (decided at compile time).
+  constexpr bool EVEN = NCK % NW == 0;
+  auto piece_is_v = [&](int u) __attribute__((always_inline)) {
+    return EVEN ? u >= NCK / NW : w + u * NW >= NCK;
+  };
+  auto piece_exists = [&](int u) __attribute__((always_inline)) {
+    return EVEN || w + u * NW < 2 * NCK;
+  };
+  uint32_t goff[QPW], loff[QPW];  // byte offsets in a pool tile / in an LDS stage
 #pragma unroll
   for (int u = 0; u < QPW; ++u) {
     const int q = w + u * NW;
@@ -378,44 +305,51 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     const int qq = isv ? q - NCK : q;
     const int row = qq * RPC + lane / (D / 8);
     const int slot = lane % (D / 8);
-    voff[u] = row * row_bytes + 16 * (isv ? v_slot<D>(row, slot) : k_slot<D>(row, slot));
+    goff[u] = row * row_bytes + 16 * slot;
+    loff[u] = (isv ? TILE * D * 2 : 0) + row * (2 * D) + 16 * (isv ? v_slot<D>(row, slot) : k_slot<D>(row, slot));
   }
-  auto issue_tile = [&](int tile_base, int stage) __attribute__((always_inline)) {
-    const uint32_t sbase = lds_base + stage * STAGE_BYTES;
+  // Each piece's address is chosen first (interior tiles: the pool segment plus a lane
+  // constant; boundary tiles: per-lane rows that may come from k_new or be clamped), then one
+  // load per piece; the staged data is kept as scalars so that it never forms one wide vector
+  // register.
+  auto load_tile = [&](int tile_base, Piece (&x)[QPW]) __attribute__((always_inline)) {
+    const char *src[QPW];
     if (tile_base + TILE <= n_fast) {
-      const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)tile_base * row_bytes);
+      const char *kt = reinterpret_cast<const char *>(kseg) + (size_t)tile_base * row_bytes;
+      const char *vt = reinterpret_cast<const char *>(vseg) + (size_t)tile_base * row_bytes;
 #pragma unroll
-      for (int u = 0; u < QPW; ++u) {
-        const int q = w + u * NW;
-        if (q < 2 * NCK) {
-          const bool isv = q >= NCK;
-          const int qq = isv ? q - NCK : q;
-          const uint32_t m0 = __builtin_amdgcn_readfirstlane(sbase + (isv ? TILE * D * 2 : 0) + qq * 1024);
-          lds_dma16_buf(m0, isv ? vrsrc : krsrc, voff[u], soff);
-        }
-      }
+      for (int u = 0; u < QPW; ++u) src[u] = (piece_is_v(u) ? vt : kt) + goff[u];
     } else {
 #pragma unroll
       for (int u = 0; u < QPW; ++u) {
         const int q = w + u * NW;
-        if (q < 2 * NCK) {
-          const bool isv = q >= NCK;
-          const int qq = isv ? q - NCK : q;
-          const int row = qq * RPC + lane / (D / 8);
-          const int slot = lane % (D / 8);
-          int pos = tile_base + row;
-          pos = pos < r_hi ? pos : r_hi - 1;  // rows past the range re-read a visible row (masked)
-          const uint16_t *src;
-          if (knew && pos >= c)
-            src = (isv ? vnew : knew) + ((int64_t)(off + pos - c) * p.hkv + g) * D;
-          else
-            src = (isv ? vseg : kseg) + (int64_t)pos * row_elems;
-          src += 8 * (isv ? v_slot<D>(row, slot) : k_slot<D>(row, slot));
-          const uint32_t m0 = __builtin_amdgcn_readfirstlane(sbase + (isv ? TILE * D * 2 : 0) + qq * 1024);
-          lds_dma16(m0, src);
-        }
+        const bool isv = piece_is_v(u);
+        const int qq = isv ? q - NCK : q;
+        const int row = qq * RPC + lane / (D / 8);
+        int pos = tile_base + row;
+        pos = pos < r_hi ? pos : r_hi - 1;  // rows past the range re-read a visible row (masked)
+        const uint16_t *r;
+        if (knew && pos >= c)
+          r = (isv ? vnew : knew) + ((int64_t)(off + pos - c) * p.hkv + g) * D;
+        else
+          r = (isv ? vseg : kseg) + (int64_t)pos * row_elems;
+        src[u] = reinterpret_cast<const char *>(r + 8 * (lane % (D / 8)));
       }
     }
+#pragma unroll
+    for (int u = 0; u < QPW; ++u) {
+      if (piece_exists(u)) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src[u]));
+        x[u] = Piece{v[0], v[1], v[2], v[3]};
+      }
+    }
+  };
+  auto store_tile = [&](const Piece (&x)[QPW], int stage) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < QPW; ++u)
+      if (piece_exists(u))
+        *(lds_u32x4 *)(uintptr_t)(lds_base + stage * STAGE_BYTES + loff[u]) =
+            u32x4{x[u].a, x[u].b, x[u].c, x[u].d};
   };
 
   // ---- lane-constant LDS operand offsets ----
@@ -526,42 +460,65 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     else
       compute_tile(base, stage_c, std::integral_constant<bool, true>{});
   };
-  if constexpr (DEEP) {
-#pragma unroll
-    for (int s = 0; s < NSTAGE - 1; ++s)
-      if (s < n_tiles) issue_tile(r_lo + s * TILE, s);
-    auto step = [&](int t, auto stage_c) __attribute__((always_inline)) {
-      constexpr int STAGE = decltype(stage_c)::value;
-      __syncthreads();  // every wave is done with the stage the next load overwrites
-      const int nxt = t + NSTAGE - 1;
-      if (nxt < n_tiles) issue_tile(r_lo + nxt * TILE, (STAGE + NSTAGE - 1) % NSTAGE);
-      wait_tiles<PER, NSTAGE>(min(NSTAGE - 1, n_tiles - 1 - t));
-      __syncthreads();  // tile t is in LDS for every wave
-      consume(r_lo + t * TILE, stage_c);
-    };
-    for (int t0 = 0; t0 < n_tiles; t0 += NSTAGE) {
-      step(t0, std::integral_constant<int, 0>{});
-      if constexpr (NSTAGE > 1) if (t0 + 1 < n_tiles) step(t0 + 1, std::integral_constant<int, 1 % NSTAGE>{});
-      if constexpr (NSTAGE > 2) if (t0 + 2 < n_tiles) step(t0 + 2, std::integral_constant<int, 2 % NSTAGE>{});
-      if constexpr (NSTAGE > 3) if (t0 + 3 < n_tiles) step(t0 + 3, std::integral_constant<int, 3 % NSTAGE>{});
-    }
+  // Tile j sits in register set j % RSETS until it is stored to LDS stage j % 2.  Iteration t
+  // consumes stage t % 2, stores tile t + 1 (its loads were issued RSETS iterations ago) to the
+  // other stage, which every wave finished reading before the previous barrier, and reuses the
+  // freed register set for tile t + 1 + RSETS.  One barrier per tile.
+  Piece xa[QPW], xb[QPW];
+  load_tile(r_lo, xa);
+  if constexpr (RSETS == 2) {
+    if (n_tiles > 1) load_tile(r_lo + TILE, xb);
+    store_tile(xa, 0);
+    if (n_tiles > 2) load_tile(r_lo + 2 * TILE, xa);
   } else {
-    static_assert(NSTAGE == 2, "the conservative schedule double-buffers");
-    issue_tile(r_lo, 0);
-    auto step = [&](int t, auto stage_c) __attribute__((always_inline)) {
-      constexpr int STAGE = decltype(stage_c)::value;
-      wait_vmcnt<0>();   // tile t (and anything else outstanding) is complete
-      __syncthreads();   // ... for every wave, and the other stage is no longer read
-      if (t + 1 < n_tiles) issue_tile(r_lo + (t + 1) * TILE, 1 - STAGE);
-      consume(r_lo + t * TILE, stage_c);
-    };
-    for (int t0 = 0; t0 < n_tiles; t0 += 2) {
-      step(t0, std::integral_constant<int, 0>{});
-      if (t0 + 1 < n_tiles) step(t0 + 1, std::integral_constant<int, 1>{});
+    store_tile(xa, 0);
+    if (n_tiles > 1) load_tile(r_lo + TILE, xa);
+  }
+  __syncthreads();
+  for (int t = 0; t < n_tiles; t += 2) {
+    consume(r_lo + t * TILE, std::integral_constant<int, 0>{});
+    if (t + 1 < n_tiles) {
+      if constexpr (RSETS == 2) {
+        store_tile(xb, 1);
+        if (t + 3 < n_tiles) load_tile(r_lo + (t + 3) * TILE, xb);
+      } else {
+        store_tile(xa, 1);
+        if (t + 2 < n_tiles) load_tile(r_lo + (t + 2) * TILE, xa);
+      }
     }
-    wait_vmcnt<0>();
+    __syncthreads();
+    if (t + 1 >= n_tiles) break;
+    consume(r_lo + (t + 1) * TILE, std::integral_constant<int, 1>{});
+    if (t + 2 < n_tiles) {
+      store_tile(xa, 0);
+      const int nxt = RSETS == 2 ? t + 4 : t + 3;
+      if (nxt < n_tiles) load_tile(r_lo + nxt * TILE, xa);
+    }
+    __syncthreads();
   }
 
+  if constexpr (!PF) {
+    // This step's KV writes, by split 0 of each (request, KV head) after its tile loop, so that
+    // they stay off the critical path (the kernel reads candidates from k_new, not from the
+    // pool): candidate j goes to pool row slot_cache_loc[off + j].
+    if (knew && split == 0) {
+      constexpr int C16 = D / 8;
+      for (int e = tid; e < nrows * C16 * 2; e += NW * 64) {
+        const int isv = e / (nrows * C16);
+        const int rem = e % (nrows * C16);
+        const int j = rem / C16, cc = rem % C16;
+        const int64_t loc = p.slot_cache_loc[off + j];
+        if (loc < 0 || loc >= p.pool_rows) {
+          status_or(p.status, DSV_STATUS_POOL);
+          continue;
+        }
+        const uint16_t *src = (isv ? vnew : knew) + ((int64_t)(off + j) * p.hkv + g) * D + cc * 8;
+        uint16_t *dst = static_cast<uint16_t *>(isv ? p.v_pool : p.k_pool) + g * p.stride_head +
+                        loc * p.stride_row + cc * 8;
+        *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
+      }
+    }
+  }
   if (!wave_live) return;
   // full row sum across the four lane groups holding the row
   l_run += __shfl_xor(l_run, 16);
@@ -616,7 +573,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   int ki, off, c;
   int64_t kb;
   if (verify_request(p, i, ki, off, c, kb) || j >= ki) return;
-  const int S = (c + ki + p.chunk - 1) / p.chunk;
+  const int S = verify_splits(p, c + ki);
   if (S <= 1) return;
   const int64_t plane = (int64_t)p.m_bs * p.hq;
   const int64_t rh = (int64_t)(off + j) * p.hq + h;
@@ -811,9 +768,12 @@ struct Plan {
   size_t ws_o = 0, ws_lse = 0;  // bytes
 };
 
-// Split plan of the verification set: KV rows per split (multiple of 64) and the number of
-// splits per request the grid provides.  Auto: aim for two workgroups per CU (512 on 256
-// CUs) when every request sits at max_ctx.
+// Split plan of the verification set: KV rows per split (multiple of 64) and the most splits
+// per request the grid provides.  Auto: aim for two workgroups per CU (512 on 256 CUs) when
+// every request sits at max_ctx, rounding the split size down to whole 64-row tiles so that
+// all splits but the last (which takes the remainder) have the same number of tiles.
+// max_ctx only shapes the plan: a longer context is still computed exactly, its last split
+// being longer.
 static Plan make_plan(const dsv_attn_args *a) {
   Plan pl;
   if (a->n_bs <= 0 || a->dtype != DSV_BF16) return pl;
@@ -824,12 +784,11 @@ static Plan make_plan(const dsv_attn_args *a) {
     int64_t target = (512 + units - 1) / units;
     if (target < 1) target = 1;
     if (target > 64) target = 64;
-    chunk = (rows + target - 1) / target;
-    chunk = (chunk + kTileKV - 1) / kTileKV * kTileKV;
+    chunk = rows / target / kTileKV * kTileKV;
     if (chunk < kTileKV) chunk = kTileKV;
   }
   pl.chunk = (int)chunk;
-  pl.n_splits = (int)((rows + chunk - 1) / chunk);
+  pl.n_splits = (int)(rows / chunk);
   if (pl.n_splits < 1) pl.n_splits = 1;
   if (pl.n_splits > 1) {
     pl.ws_o = align256((size_t)pl.n_splits * a->m_bs * a->hq * a->d * sizeof(float));
@@ -838,20 +797,17 @@ static Plan make_plan(const dsv_attn_args *a) {
   return pl;
 }
 
-// Tile rows and ring depth per head_dim: 2-stage rings of 32 KB stages (16 KB for D = 64),
-// two workgroups per CU.
+// Tile rows per head_dim (two LDS stages of K and V tiles: 32 KB for D = 128).
 template <int D> struct TileCfg;
-template <> struct TileCfg<64> { static constexpr int TILE = 64, VSTAGES = 4, PSTAGES = 4; };
-template <> struct TileCfg<128> { static constexpr int TILE = 64, VSTAGES = 2, PSTAGES = 2; };
-template <> struct TileCfg<256> { static constexpr int TILE = 32, VSTAGES = 2, PSTAGES = 2; };
+template <> struct TileCfg<64> { static constexpr int TILE = 64; };
+template <> struct TileCfg<128> { static constexpr int TILE = 64; };
+template <> struct TileCfg<256> { static constexpr int TILE = 32; };
 
 template <int D, int NW, bool PF>
 static bool launch_attn(const AttnParams &p, int grid, hipStream_t s) {
   constexpr int TILE = TileCfg<D>::TILE;
-  constexpr bool DEEP = deep_schedule<D, NW>();
-  constexpr int NSTAGE = DEEP ? (PF ? TileCfg<D>::PSTAGES : TileCfg<D>::VSTAGES) : 2;
-  constexpr size_t shm = (size_t)NSTAGE * 2 * TILE * D * sizeof(uint16_t);
-  auto kern = attn_bf16_kernel<D, NW, PF, TILE, NSTAGE, DEEP>;
+  constexpr size_t shm = (size_t)2 * 2 * TILE * D * sizeof(uint16_t);
+  auto kern = attn_bf16_kernel<D, NW, PF, TILE>;
   // once per kernel (idempotent), so that a captured call contains launches only
   static bool lds_limit_set = false;
   if (!lds_limit_set) {

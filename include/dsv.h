@@ -61,8 +61,7 @@ typedef enum dsv_dtype {
 #define DSV_STATUS_BAD_REQUEST 1 /* k_i outside [0, W], negative context/base, offsets out of range */
 #define DSV_STATUS_BUDGET 2      /* sum of k_i exceeds the slot capacity m_bs */
 #define DSV_STATUS_NAN 4         /* a NaN logit */
-#define DSV_STATUS_POOL 8        /* a visible KV row or a candidate write outside the pool, or a
-                                    context longer than the split plan (max_ctx) allows */
+#define DSV_STATUS_POOL 8        /* a visible KV row or a candidate write outside the pool */
 #define DSV_STATUS_PREFILL 16    /* a prefill request outside its declared bounds */
 
 /* Largest candidate block width (anchor included) the verification tile covers. */
@@ -124,7 +123,9 @@ dsv_status dsv_pack_slots(int32_t n_bs, int32_t W, int32_t m_bs, const int32_t *
 /* offsets[i] + j); they are used for the candidate positions and written   */
 /* to pool rows slot_cache_loc[offsets[i] + j] (this step's KV writes).  If  */
 /* they are null the candidates are read from pool rows kv_base[i] +         */
-/* ctx_len[i] + j.                                                           */
+/* ctx_len[i] + j.  A cache reference must not be a row that some request    */
+/* of the same call reads from the pool (its committed context): such reads  */
+/* would race with the write.                                                */
 /*                                                                            */
 /* Prefill set (optional, n_pf > 0).  Request r has pf_q_len[r] query rows   */
 /* at rows pf_q_start[r] + j of pf_q at positions pf_ctx_len[r] + j; every   */
@@ -146,7 +147,7 @@ dsv_status dsv_pack_slots(int32_t n_bs, int32_t W, int32_t m_bs, const int32_t *
 /* Supported: d in {64, 128, 256}; hq % hkv == 0; hq / hkv <= 16 (bf16);     */
 /*   W <= DSV_MAX_W.                                                          */
 /* Errors (device): invalid request (k_i outside [0, W], negative ctx/base,  */
-/*   offsets[i] + k_i > m_bs, segment past pool_rows, ctx_len[i] > max_ctx): */
+/*   offsets[i] + k_i > m_bs, segment past pool_rows):                      */
 /*   DSV_STATUS_BAD_REQUEST or DSV_STATUS_POOL, its rows are zero-filled     */
 /*   when its offsets are in range; a candidate write outside the pool is    */
 /*   skipped with DSV_STATUS_POOL; invalid prefill request:                  */
@@ -157,7 +158,9 @@ typedef struct dsv_attn_args {
   int32_t hq, hkv, d;
   float softmax_scale; /* 0 => 1 / sqrt(d) */
   int32_t kv_chunk;    /* KV rows per split of a verification request (multiple of 64); 0 => auto */
-  int32_t max_ctx;     /* host-known upper bound of every ctx_len[i] of the verification set */
+  int32_t max_ctx;     /* host-known typical/upper context length of the verification set: sizes
+                          the split plan and the workspace; a longer ctx_len[i] is still
+                          computed exactly (its last split is longer) */
 
   /* KV pool (written at candidate rows) */
   void *k_pool, *v_pool;
