@@ -34,7 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-PROFILED_KERNEL = "attn_bf16_kernel<128, 4, false>"
+PROFILED_KERNEL = "attn_bf16_kernel<128, 8, false, 64, 2>"
 
 
 class HipEvents:

@@ -69,6 +69,7 @@ struct AttnParams {
   void *pf_out;
   float *pf_lse;
   int32_t *status;
+
 };
 
 // Checks request i of the verification set; on success returns 0 and its fields.
@@ -117,11 +118,11 @@ __device__ void zero_rows_bf16(uint16_t *out, float *lse, int hq, int r0, int r1
     int64_t t = e / C;
     int hh = (int)(t % nh);
     int r = r0 + (int)(t / nh);
-    *reinterpret_cast<uint4 *>(out + ((int64_t)r * hq + h0 + hh) * D + cc * 8) = make_uint4(0, 0, 0, 0);
+    gstore(out + ((int64_t)r * hq + h0 + hh) * D + cc * 8, u32x4{0u, 0u, 0u, 0u});
   }
   if (lse)
     for (int64_t e = tid; e < (int64_t)(r1 - r0) * nh; e += nt)
-      lse[(int64_t)(r0 + e / nh) * hq + h0 + e % nh] = -INFINITY;
+      gstore(lse + (int64_t)(r0 + e / nh) * hq + h0 + e % nh, -INFINITY);
 }
 
 // ---------------------------------------------------------------------------
@@ -132,7 +133,6 @@ __device__ void zero_rows_bf16(uint16_t *out, float *lse, int hq, int r0, int r1
 // tracks completion of the register loads.  (Direct global->LDS loads, measured on the same
 // access pattern, sustained about 12% less bandwidth than loads through registers.)
 // ---------------------------------------------------------------------------
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 struct Piece {  // 16 staged bytes
   uint32_t a, b, c, d;
@@ -181,17 +181,20 @@ constexpr int waves_per_eu_hint() {
   return (NW <= 2 || (D == 256 && NW <= 4)) ? 1 : (NW <= 8 ? 2 : 1);
 }
 
-template <int D, int NW, bool PF, int TILE>
+template <int D, int NW, bool PF, int TILE, int HV>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_per_eu_hint<D, NW>()))) void attn_bf16_kernel(AttnParams p) {
   constexpr int RPC = 1024 / (2 * D);        // rows per 1 KB wave load
   constexpr int NCK = TILE / RPC;            // wave loads per tensor per tile
-  constexpr int QPW = (2 * NCK + NW - 1) / NW;  // wave loads per wave per tile (at most)
-  constexpr int RSETS = QPW <= kTwoSetMaxLoads ? 2 : 1;  // register sets (tiles in flight besides LDS)
-  constexpr int STAGE_BYTES = 2 * TILE * D * 2;
+  constexpr int NP = 2 * NCK * HV;           // wave loads per stage (HV tiles of K and V)
+  constexpr int QPW = (NP + NW - 1) / NW;    // wave loads per wave per stage (at most)
+  constexpr int RSETS = QPW <= kTwoSetMaxLoads ? 2 : 1;  // register sets (stages in flight besides LDS)
+  constexpr int SUB_BYTES = 2 * TILE * D * 2;  // one tile of K and V
+  constexpr int STAGE_BYTES = HV * SUB_BYTES;
+  constexpr int NWH = NW / HV;               // waves per KV half
+  static_assert(!PF || HV == 1, "prefill stacks its waves along the query rows");
+  static_assert(NW % HV == 0, "wave halves");
   constexpr int DB = D / 16;
   constexpr int KS = D / 32;
-  constexpr int KB = TILE / 16;              // 16-row score blocks per tile
-  constexpr int KK = TILE / 32;              // 32-row P.V steps per tile
   static_assert(TILE % 32 == 0 && TILE % RPC == 0, "tile shape");
 
   extern __shared__ __align__(16) uint16_t lds[];
@@ -200,6 +203,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int lq = lane & 15, lg = lane >> 4;
+  // KV half of this wave (HV = 2: waves [0, NWH) consume the even tiles of each stage pair,
+  // waves [NWH, NW) the odd ones, for the same query heads) and its head within the group
+  const int half = HV == 1 ? 0 : w / NWH;
+  const int wh = HV == 1 ? w : w - half * NWH;
 
   // ---- work unit ----
   int g, h, c, r_lo, r_hi, row0, nrows, split = 0, n_splits_i = 1, off = 0;
@@ -212,7 +219,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     const int t = bid / p.hkv;
     const int i = t % p.n_bs;
     split = t / p.n_bs;
-    h = g * p.G + w;
+    h = g * p.G + wh;
     if (i == 0 && split == 0) {
       int end = p.offsets[p.n_bs];
       end = end < 0 ? 0 : (end > p.m_bs ? p.m_bs : end);
@@ -274,7 +281,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     const uint16_t *qp = qsrc + ((q_row0 + (ok ? my_row : 0)) * p.hq + h) * (int64_t)D + 8 * lg;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      uint4 v = ok ? *reinterpret_cast<const uint4 *>(qp + 32 * ks) : make_uint4(0, 0, 0, 0);
+      const u32x4 v = ok ? gload<u32x4>(qp + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
       qf[ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -286,27 +293,39 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
   const uint32_t row_bytes = (uint32_t)(row_elems * 2);
   const uint16_t *kseg = static_cast<const uint16_t *>(p.k_pool) + g * p.stride_head + kb * row_elems;
   const uint16_t *vseg = static_cast<const uint16_t *>(p.v_pool) + g * p.stride_head + kb * row_elems;
-  // rows [0, n_fast) of the request come from the pool; interior tiles lie below it
-  const int n_fast = knew ? min(r_hi, c) : r_hi;
-  // With NCK a multiple of NW every wave moves the same pieces pattern: its first NCK / NW
-  // pieces are K, the rest V, and none is past the tile (decided at compile time).
+  // Verification: the tile loop covers the committed rows [r_lo, t_hi) from the pool; the
+  // candidate positions [c, c + k_i) (all in the request's last split) form a separate
+  // candidate block, staged with the first tile and consumed before the loop, so the split
+  // that holds them runs no extra pipeline iteration.  Prefill: the loop covers everything.
+  const bool has_cand = !PF && r_hi > c;
+  const int t_hi = has_cand ? c : r_hi;
+  // Piece q of a stage: tile q / (2 NCK) of the stage, K if q % (2 NCK) < NCK else V, rows
+  // RPC (q % NCK) ..  With NCK a multiple of NW every wave moves the same pattern (which tile,
+  // K or V, and no piece past the stage: decided at compile time).
   constexpr bool EVEN = NCK % NW == 0;
+  auto piece_sub = [&](int u) __attribute__((always_inline)) {
+    return EVEN ? u / (2 * NCK / NW) : (w + u * NW) / (2 * NCK);
+  };
   auto piece_is_v = [&](int u) __attribute__((always_inline)) {
-    return EVEN ? u >= NCK / NW : w + u * NW >= NCK;
+    return EVEN ? u % (2 * NCK / NW) >= NCK / NW : (w + u * NW) % (2 * NCK) >= NCK;
   };
   auto piece_exists = [&](int u) __attribute__((always_inline)) {
-    return EVEN || w + u * NW < 2 * NCK;
+    return EVEN || w + u * NW < NP;
   };
-  uint32_t goff[QPW], loff[QPW];  // byte offsets in a pool tile / in an LDS stage
+  // row of piece u within its tile
+  auto piece_row = [&](int u) __attribute__((always_inline)) {
+    return ((w + u * NW) % NCK) * RPC + lane / (D / 8);
+  };
+  uint32_t goff[QPW], loff[QPW];  // byte offsets in a pool stage / in an LDS stage
 #pragma unroll
   for (int u = 0; u < QPW; ++u) {
-    const int q = w + u * NW;
-    const bool isv = q >= NCK;
-    const int qq = isv ? q - NCK : q;
-    const int row = qq * RPC + lane / (D / 8);
+    const bool isv = piece_is_v(u);
+    const int sub = piece_sub(u);
+    const int row = piece_row(u);
     const int slot = lane % (D / 8);
-    goff[u] = row * row_bytes + 16 * slot;
-    loff[u] = (isv ? TILE * D * 2 : 0) + row * (2 * D) + 16 * (isv ? v_slot<D>(row, slot) : k_slot<D>(row, slot));
+    goff[u] = (sub * TILE + row) * row_bytes + 16 * slot;
+    loff[u] = sub * SUB_BYTES + (isv ? TILE * D * 2 : 0) + row * (2 * D) +
+              16 * (isv ? v_slot<D>(row, slot) : k_slot<D>(row, slot));
   }
   // Each piece's address is chosen first (interior tiles: the pool segment plus a lane
   // constant; boundary tiles: per-lane rows that may come from k_new or be clamped), then one
@@ -314,7 +333,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
   // register.
   auto load_tile = [&](int tile_base, Piece (&x)[QPW]) __attribute__((always_inline)) {
     const char *src[QPW];
-    if (tile_base + TILE <= n_fast) {
+    if (tile_base + HV * TILE <= t_hi) {
       const char *kt = reinterpret_cast<const char *>(kseg) + (size_t)tile_base * row_bytes;
       const char *vt = reinterpret_cast<const char *>(vseg) + (size_t)tile_base * row_bytes;
 #pragma unroll
@@ -322,24 +341,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     } else {
 #pragma unroll
       for (int u = 0; u < QPW; ++u) {
-        const int q = w + u * NW;
         const bool isv = piece_is_v(u);
-        const int qq = isv ? q - NCK : q;
-        const int row = qq * RPC + lane / (D / 8);
-        int pos = tile_base + row;
-        pos = pos < r_hi ? pos : r_hi - 1;  // rows past the range re-read a visible row (masked)
-        const uint16_t *r;
-        if (knew && pos >= c)
-          r = (isv ? vnew : knew) + ((int64_t)(off + pos - c) * p.hkv + g) * D;
-        else
-          r = (isv ? vseg : kseg) + (int64_t)pos * row_elems;
+        int pos = tile_base + piece_sub(u) * TILE + piece_row(u);
+        pos = pos < t_hi ? pos : t_hi - 1;  // rows past the range re-read a visible row (masked)
+        const uint16_t *r = (isv ? vseg : kseg) + (int64_t)pos * row_elems;
         src[u] = reinterpret_cast<const char *>(r + 8 * (lane % (D / 8)));
       }
     }
 #pragma unroll
     for (int u = 0; u < QPW; ++u) {
       if (piece_exists(u)) {
-        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src[u]));
+        const u32x4 v = gload_stream<u32x4>(src[u]);
         x[u] = Piece{v[0], v[1], v[2], v[3]};
       }
     }
@@ -356,15 +368,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
   // K (A operand of S^T): row 16kb + lq, slot 4ks + lg
   uint32_t koff[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) koff[ks] = lds_base + lq * (2 * D) + k_slot<D>(lq, 4 * ks + lg) * 16;
+  for (int ks = 0; ks < KS; ++ks)
+    koff[ks] = lds_base + half * SUB_BYTES + lq * (2 * D) + k_slot<D>(lq, 4 * ks + lg) * 16;
   // V (transposing reads): row R + lq/4 with R = 32kk + 16half + 4lg, 8 bytes at column
   // 16db + 4(lq%4); the row term 32kk + 16half does not change the swizzle
   uint32_t voffs[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
     const int row = 4 * lg + (lq >> 2);
-    voffs[db] = lds_base + TILE * D * 2 + row * (2 * D) + v_slot<D>(row, 2 * db + ((lq & 3) >> 1)) * 16 +
-                8 * (lq & 1);
+    voffs[db] = lds_base + half * SUB_BYTES + TILE * D * 2 + row * (2 * D) +
+                v_slot<D>(row, 2 * db + ((lq & 3) >> 1)) * 16 + 8 * (lq & 1);
   }
 
   f32x4 acc_o[DB];
@@ -372,14 +385,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
   for (int db = 0; db < DB; ++db) acc_o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY, l_run = 0.f;  // reference max (log2 units) and row-sum partial
 
-  const int n_tiles = (r_hi - r_lo + TILE - 1) / TILE;
+  const int n_tiles = (t_hi - r_lo + HV * TILE - 1) / (HV * TILE);  // stages of HV tiles
   const int wave_row_lo = PF ? row0 + w * 16 : 0;
   const bool wave_live = wave_row_lo < nrows;
   const float sl2 = p.scale_log2;
 
-  auto compute_tile = [&](int base, auto stage_c, auto mask_c) __attribute__((always_inline)) {
+  // One tile of ROWS (TILE, or 32 for the candidate block) KV rows at positions base.. from
+  // LDS stage STAGE; with MASK, positions at or past hi or past the row's last visible position
+  // are excluded.
+  auto compute_tile = [&](int base, int hi, auto stage_c, auto mask_c, auto rows_c) __attribute__((always_inline)) {
     constexpr int STAGE = decltype(stage_c)::value;
     constexpr bool MASK = decltype(mask_c)::value;
+    constexpr int ROWS = decltype(rows_c)::value;
+    constexpr int KB = ROWS / 16;  // 16-row score blocks
+    constexpr int KK = ROWS / 32;  // 32-row P.V steps
     // S^T blocks: acc_s[kb][e] = raw score of KV row base + 16kb + 4lg + e for query row lq
     f32x4 acc_s[KB];
 #pragma unroll
@@ -392,21 +411,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
         acc_s[kbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], acc_s[kbk], 0, 0, 0);
       }
     }
-    float mt = -INFINITY;
+    float mt = -INFINITY;  // this lane's maximum over its entries of the row
 #pragma unroll
     for (int kbk = 0; kbk < KB; ++kbk)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         if constexpr (MASK) {
           const int pos = base + 16 * kbk + 4 * lg + e;
-          acc_s[kbk][e] = (pos < r_hi && pos <= lim) ? acc_s[kbk][e] : -INFINITY;
+          acc_s[kbk][e] = (pos < hi && pos <= lim) ? acc_s[kbk][e] : -INFINITY;
         }
         mt = fmaxf(mt, acc_s[kbk][e]);
       }
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mt2 = mt * sl2;  // tile max in log2 units (-inf if fully masked)
-    if (__builtin_expect(__any(mt2 > m_ref + kRescaleSlack), 0)) {
+    // The reference moves only when some entry of a row exceeds it by more than the slack.
+    // Whether any does is decided per lane (a ballot); the row maximum over the four lanes
+    // holding the row is formed only then.
+    if (__builtin_expect(__any(mt * sl2 > m_ref + kRescaleSlack), 0)) {
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float mt2 = mt * sl2;  // row maximum of the tile in log2 units (-inf if masked)
       const float m_new = mt2 > m_ref + kRescaleSlack ? mt2 : m_ref;
       // rows that have seen no visible key yet hold zeros: their factor is 0 (not NaN)
       const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
@@ -453,46 +475,100 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
   };
 
   // rows of this wave that can see any key of tile `base`; interior tiles skip the mask
-  auto consume = [&](int base, auto stage_c) __attribute__((always_inline)) {
+  auto consume = [&](int stage_base, auto stage_c) __attribute__((always_inline)) {
+    const int base = stage_base + half * TILE;
+    if (HV > 1 && base >= t_hi) return;                     // this half's tile is past the range
     if (!wave_live || base > c + wave_row_lo + 15) return;  // past every row's last position
-    if (base + TILE - 1 <= c + wave_row_lo && base + TILE <= r_hi)
-      compute_tile(base, stage_c, std::integral_constant<bool, false>{});
+    using Rows = std::integral_constant<int, TILE>;
+    if (base + TILE - 1 <= c + wave_row_lo && base + TILE <= t_hi)
+      compute_tile(base, t_hi, stage_c, std::integral_constant<bool, false>{}, Rows{});
     else
-      compute_tile(base, stage_c, std::integral_constant<bool, true>{});
+      compute_tile(base, t_hi, stage_c, std::integral_constant<bool, true>{}, Rows{});
   };
+
+  // Candidate block: K and V rows 0 .. k_i - 1 (from k_new, else from the pool) in the layout of
+  // a 32-row tile of LDS stage 1, V rows k_i .. 31 zero (they meet zero probabilities in the
+  // 32-row P.V step).  Loaded in one batch per thread.
+  constexpr int CPH = 2 * 16 * (D / 8);  // pieces of K and V rows 0..15
+  constexpr int CPB = (CPH + NW * 64 - 1) / (NW * 64);
+  auto stage_candidates = [&]() __attribute__((always_inline)) {
+    Piece xc[CPB];
+#pragma unroll
+    for (int b = 0; b < CPB; ++b) {
+      const int e = b * NW * 64 + tid;
+      const int isv = e / (16 * (D / 8)), row = (e / (D / 8)) % 16, slot = e % (D / 8);
+      xc[b] = Piece{0u, 0u, 0u, 0u};
+      if (e < CPH && row < nrows) {
+        const uint16_t *r = knew ? (isv ? vnew : knew) + ((int64_t)(off + row) * p.hkv + g) * D
+                                 : (isv ? vseg : kseg) + (int64_t)(c + row) * row_elems;
+        const u32x4 v = gload_stream<u32x4>(r + 8 * slot);
+        xc[b] = Piece{v[0], v[1], v[2], v[3]};
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < CPB; ++b) {
+      const int e = b * NW * 64 + tid;
+      const int isv = e / (16 * (D / 8)), row = (e / (D / 8)) % 16, slot = e % (D / 8);
+      if (e < CPH)
+        *(lds_u32x4 *)(uintptr_t)(lds_base + STAGE_BYTES + (isv ? TILE * D * 2 : 0) + row * (2 * D) +
+                                  16 * (isv ? v_slot<D>(row, slot) : k_slot<D>(row, slot))) =
+            u32x4{xc[b].a, xc[b].b, xc[b].c, xc[b].d};
+    }
+    for (int e = tid; e < 16 * (D / 8); e += NW * 64) {
+      const int row = 16 + e / (D / 8), slot = e % (D / 8);
+      *(lds_u32x4 *)(uintptr_t)(lds_base + STAGE_BYTES + TILE * D * 2 + row * (2 * D) +
+                                16 * v_slot<D>(row, slot)) = u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+
   // Tile j sits in register set j % RSETS until it is stored to LDS stage j % 2.  Iteration t
   // consumes stage t % 2, stores tile t + 1 (its loads were issued RSETS iterations ago) to the
   // other stage, which every wave finished reading before the previous barrier, and reuses the
   // freed register set for tile t + 1 + RSETS.  One barrier per tile.
   Piece xa[QPW], xb[QPW];
-  load_tile(r_lo, xa);
-  if constexpr (RSETS == 2) {
-    if (n_tiles > 1) load_tile(r_lo + TILE, xb);
-    store_tile(xa, 0);
-    if (n_tiles > 2) load_tile(r_lo + 2 * TILE, xa);
-  } else {
-    store_tile(xa, 0);
-    if (n_tiles > 1) load_tile(r_lo + TILE, xa);
+  if (n_tiles > 0) load_tile(r_lo, xa);
+  if constexpr (!PF) {
+    if (has_cand) {
+      stage_candidates();  // into stage 1, which the loop first writes after a barrier
+      if (n_tiles > 0) store_tile(xa, 0);
+      if (n_tiles > 1) load_tile(r_lo + (HV * TILE), RSETS == 2 ? xb : xa);
+      if (RSETS == 2 && n_tiles > 2) load_tile(r_lo + 2 * (HV * TILE), xa);
+      __syncthreads();
+      if (wave_live && half == 0)
+        compute_tile(c, r_hi, std::integral_constant<int, 1>{}, std::integral_constant<bool, true>{},
+                     std::integral_constant<int, 32>{});
+      __syncthreads();
+    }
   }
-  __syncthreads();
+  if (!has_cand) {
+    if constexpr (RSETS == 2) {
+      if (n_tiles > 1) load_tile(r_lo + (HV * TILE), xb);
+      if (n_tiles > 0) store_tile(xa, 0);
+      if (n_tiles > 2) load_tile(r_lo + 2 * (HV * TILE), xa);
+    } else {
+      if (n_tiles > 0) store_tile(xa, 0);
+      if (n_tiles > 1) load_tile(r_lo + (HV * TILE), xa);
+    }
+    __syncthreads();
+  }
   for (int t = 0; t < n_tiles; t += 2) {
-    consume(r_lo + t * TILE, std::integral_constant<int, 0>{});
+    consume(r_lo + t * (HV * TILE), std::integral_constant<int, 0>{});
     if (t + 1 < n_tiles) {
       if constexpr (RSETS == 2) {
         store_tile(xb, 1);
-        if (t + 3 < n_tiles) load_tile(r_lo + (t + 3) * TILE, xb);
+        if (t + 3 < n_tiles) load_tile(r_lo + (t + 3) * (HV * TILE), xb);
       } else {
         store_tile(xa, 1);
-        if (t + 2 < n_tiles) load_tile(r_lo + (t + 2) * TILE, xa);
+        if (t + 2 < n_tiles) load_tile(r_lo + (t + 2) * (HV * TILE), xa);
       }
     }
     __syncthreads();
     if (t + 1 >= n_tiles) break;
-    consume(r_lo + (t + 1) * TILE, std::integral_constant<int, 1>{});
+    consume(r_lo + (t + 1) * (HV * TILE), std::integral_constant<int, 1>{});
     if (t + 2 < n_tiles) {
       store_tile(xa, 0);
       const int nxt = RSETS == 2 ? t + 4 : t + 3;
-      if (nxt < n_tiles) load_tile(r_lo + nxt * TILE, xa);
+      if (nxt < n_tiles) load_tile(r_lo + nxt * (HV * TILE), xa);
     }
     __syncthreads();
   }
@@ -515,9 +591,36 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
         const uint16_t *src = (isv ? vnew : knew) + ((int64_t)(off + j) * p.hkv + g) * D + cc * 8;
         uint16_t *dst = static_cast<uint16_t *>(isv ? p.v_pool : p.k_pool) + g * p.stride_head +
                         loc * p.stride_row + cc * 8;
-        *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
+        gstore(dst, gload<u32x4>(src));
       }
     }
+  }
+  if constexpr (HV == 2) {
+    // The two halves hold online-softmax states over disjoint tiles of the same rows: half 1
+    // hands its state to half 0 through LDS (unused after the loop's last barrier), half 0
+    // merges them.  Layout [value][wave][lane], conflict-free.
+    float *xs = reinterpret_cast<float *>(lds);
+    auto at = [&](int k) __attribute__((always_inline)) { return (k * NWH + wh) * 64 + lane; };
+    if (half == 1) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xs[at(4 * db + e)] = acc_o[db][e];
+      xs[at(4 * DB)] = m_ref;
+      xs[at(4 * DB + 1)] = l_run;
+    }
+    __syncthreads();
+    if (half == 1) return;
+    const float m1 = xs[at(4 * DB)], l1 = xs[at(4 * DB + 1)];
+    const float m_new = fmaxf(m_ref, m1);
+    const float a0 = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m_new);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc_o[db][e] = acc_o[db][e] * a0 + xs[at(4 * db + e)] * a1;
+    l_run = l_run * a0 + l1 * a1;
+    m_ref = m_new;
   }
   if (!wave_live) return;
   // full row sum across the four lane groups holding the row
@@ -533,23 +636,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int d = 16 * db + 4 * lg;
-      uint2 v;
-      v.x = cvt_pk_bf16(acc_o[db][0] * inv_l, acc_o[db][1] * inv_l);
-      v.y = cvt_pk_bf16(acc_o[db][2] * inv_l, acc_o[db][3] * inv_l);
-      *reinterpret_cast<uint2 *>(o + d) = v;
+      gstore(o + d, u32x2{cvt_pk_bf16(acc_o[db][0] * inv_l, acc_o[db][1] * inv_l),
+                          cvt_pk_bf16(acc_o[db][2] * inv_l, acc_o[db][3] * inv_l)});
     }
     float *lse = PF ? p.pf_lse : p.lse;
-    if (lse && lg == 0) lse[orow * p.hq + h] = lse_v;
+    if (lse && lg == 0) gstore(lse + orow * p.hq + h, lse_v);
   } else {
+    // partials are read once, by the merge kernel: streaming (non-temporal) stores
     float *o = p.ws_o + (((int64_t)split * p.m_bs + orow) * p.hq + h) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int d = 16 * db + 4 * lg;
-      *reinterpret_cast<float4 *>(o + d) =
-          make_float4(acc_o[db][0] * inv_l, acc_o[db][1] * inv_l, acc_o[db][2] * inv_l,
-                      acc_o[db][3] * inv_l);
+      gstore_stream(o + d, f32x4{acc_o[db][0] * inv_l, acc_o[db][1] * inv_l, acc_o[db][2] * inv_l,
+                                 acc_o[db][3] * inv_l});
     }
-    if (lg == 0) p.ws_lse[((int64_t)split * p.m_bs + orow) * p.hq + h] = lse_v;
+    if (lg == 0) gstore_stream(p.ws_lse + ((int64_t)split * p.m_bs + orow) * p.hq + h, lse_v);
   }
 }
 
@@ -579,29 +680,25 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   const int64_t rh = (int64_t)(off + j) * p.hq + h;
   // one pass with a running maximum; the loads of up to eight splits are issued together
   float M = -INFINITY, den = 0.f;
-  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-  const float4 *src = reinterpret_cast<const float4 *>(p.ws_o + rh * D) + l4;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  const f32x4 *src = reinterpret_cast<const f32x4 *>(p.ws_o + rh * D) + l4;
   const int64_t step4 = plane * D / 4;
 #pragma unroll 8
   for (int s = 0; s < S; ++s) {
-    const float ls = p.ws_lse[s * plane + rh];
-    const float4 o = src[s * step4];
+    const float ls = gload<float>(p.ws_lse + s * plane + rh);
+    const f32x4 o = gload<f32x4>(src + s * step4);
     const float m_new = fmaxf(M, ls);
     const float a = m_new == -INFINITY ? 1.f : __expf(M - m_new);   // rescale of the sum so far
     const float b = ls == -INFINITY ? 0.f : __expf(ls - m_new);     // weight of split s
     den = den * a + b;
-    num.x = num.x * a + b * o.x;
-    num.y = num.y * a + b * o.y;
-    num.z = num.z * a + b * o.z;
-    num.w = num.w * a + b * o.w;
+    num = num * a + b * o;
     M = m_new;
   }
   const float inv = 1.f / den;
-  uint2 v;
-  v.x = f32_to_bf16_bits(num.x * inv) | (f32_to_bf16_bits(num.y * inv) << 16);
-  v.y = f32_to_bf16_bits(num.z * inv) | (f32_to_bf16_bits(num.w * inv) << 16);
-  *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.out) + rh * D + 4 * l4) = v;
-  if (l4 == 0 && p.lse) p.lse[rh] = M + __logf(den);
+  const u32x2 v = {f32_to_bf16_bits(num[0] * inv) | (f32_to_bf16_bits(num[1] * inv) << 16),
+                   f32_to_bf16_bits(num[2] * inv) | (f32_to_bf16_bits(num[3] * inv) << 16)};
+  gstore(static_cast<uint16_t *>(p.out) + rh * D + 4 * l4, v);
+  if (l4 == 0 && p.lse) gstore(p.lse + rh, M + __logf(den));
 }
 
 // ---------------------------------------------------------------------------
@@ -768,10 +865,16 @@ struct Plan {
   size_t ws_o = 0, ws_lse = 0;  // bytes
 };
 
+// KV halves per verification workgroup: groups of up to 4 query heads run two halves of
+// G waves each (one 8-wave workgroup per CU for G = 4), larger groups one.
+static int verify_halves(int G) { return G <= 4 ? 2 : 1; }
+
 // Split plan of the verification set: KV rows per split (multiple of 64) and the most splits
-// per request the grid provides.  Auto: aim for two workgroups per CU (512 on 256 CUs) when
-// every request sits at max_ctx, rounding the split size down to whole 64-row tiles so that
-// all splits but the last (which takes the remainder) have the same number of tiles.
+// per request the grid provides.  Auto: aim for 512 wave groups (G waves, one per query head
+// of the group) in flight, two per SIMD on 256 CUs: 512 single-half or 256 two-half
+// workgroups, when every request
+// sits at max_ctx, rounding the split size down to whole 64-row tiles so that all splits but
+// the last (which takes the remainder) have the same number of tiles.
 // max_ctx only shapes the plan: a longer context is still computed exactly, its last split
 // being longer.
 static Plan make_plan(const dsv_attn_args *a) {
@@ -781,7 +884,8 @@ static Plan make_plan(const dsv_attn_args *a) {
   int64_t chunk = a->kv_chunk;
   if (chunk <= 0) {
     const int64_t units = (int64_t)a->n_bs * a->hkv;
-    int64_t target = (512 + units - 1) / units;
+    const int64_t wgs = 512 / verify_halves(a->hkv > 0 ? a->hq / a->hkv : 1);
+    int64_t target = (wgs + units - 1) / units;
     if (target < 1) target = 1;
     if (target > 64) target = 64;
     chunk = rows / target / kTileKV * kTileKV;
@@ -797,17 +901,17 @@ static Plan make_plan(const dsv_attn_args *a) {
   return pl;
 }
 
-// Tile rows per head_dim (two LDS stages of K and V tiles: 32 KB for D = 128).
+// Tile rows per head_dim.  LDS: two stages of HV tiles of K and V (32 KB per tile for D = 128).
 template <int D> struct TileCfg;
 template <> struct TileCfg<64> { static constexpr int TILE = 64; };
 template <> struct TileCfg<128> { static constexpr int TILE = 64; };
 template <> struct TileCfg<256> { static constexpr int TILE = 32; };
 
-template <int D, int NW, bool PF>
+template <int D, int NW, bool PF, int HV = 1>
 static bool launch_attn(const AttnParams &p, int grid, hipStream_t s) {
   constexpr int TILE = TileCfg<D>::TILE;
-  constexpr size_t shm = (size_t)2 * 2 * TILE * D * sizeof(uint16_t);
-  auto kern = attn_bf16_kernel<D, NW, PF, TILE>;
+  constexpr size_t shm = (size_t)2 * HV * 2 * TILE * D * sizeof(uint16_t);
+  auto kern = attn_bf16_kernel<D, NW, PF, TILE, HV>;
   // once per kernel (idempotent), so that a captured call contains launches only
   static bool lds_limit_set = false;
   if (!lds_limit_set) {
@@ -822,11 +926,12 @@ static bool launch_attn(const AttnParams &p, int grid, hipStream_t s) {
 
 template <int D>
 static int launch_verify_g(const AttnParams &p, int grid, hipStream_t s) {
+  // groups of up to 4 heads: two KV halves (verify_halves)
   switch (p.G) {
-    case 1: return launch_attn<D, 1, false>(p, grid, s);
-    case 2: return launch_attn<D, 2, false>(p, grid, s);
-    case 3: return launch_attn<D, 3, false>(p, grid, s);
-    case 4: return launch_attn<D, 4, false>(p, grid, s);
+    case 1: return launch_attn<D, 2, false, 2>(p, grid, s);
+    case 2: return launch_attn<D, 4, false, 2>(p, grid, s);
+    case 3: return launch_attn<D, 6, false, 2>(p, grid, s);
+    case 4: return launch_attn<D, 8, false, 2>(p, grid, s);
     case 5: return launch_attn<D, 5, false>(p, grid, s);
     case 6: return launch_attn<D, 6, false>(p, grid, s);
     case 7: return launch_attn<D, 7, false>(p, grid, s);

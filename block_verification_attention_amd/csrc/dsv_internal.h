@@ -10,6 +10,8 @@ namespace dsv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -73,6 +75,29 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     v = o > v ? o : v;
   }
   return v;
+}
+
+// Global-memory accesses through address-space-qualified pointers.  Pointers that reach a
+// kernel inside a by-value parameter struct are generic to the compiler, which then emits
+// flat instructions for them; a flat load also counts against the LDS counter, so every LDS
+// wait would wait for outstanding HBM loads too.  T is a scalar or an ext_vector_type.
+template <class T>
+using global_t = __attribute__((address_space(1))) T;
+template <class T>
+__device__ __forceinline__ T gload(const void *ptr) {
+  return *(const global_t<T> *)ptr;
+}
+template <class T>
+__device__ __forceinline__ T gload_stream(const void *ptr) {  // read once: non-temporal
+  return __builtin_nontemporal_load((const global_t<T> *)ptr);
+}
+template <class T>
+__device__ __forceinline__ void gstore(void *ptr, T v) {
+  *(global_t<T> *)ptr = v;
+}
+template <class T>
+__device__ __forceinline__ void gstore_stream(void *ptr, T v) {  // read once later: non-temporal
+  __builtin_nontemporal_store(v, (global_t<T> *)ptr);
 }
 
 __device__ __forceinline__ void status_or(int32_t *status, int32_t bits) {
