@@ -250,10 +250,14 @@ dsv_status dsv_accept(int32_t n_bs, int32_t m_bs, int32_t W, int32_t vocab,
 /* dsv_probe_stream_read -- measurement helper (not part of the method)      */
 /*                                                                            */
 /* Reads `bytes` (rounded down to 16) of device memory at `buf` (16-byte     */
-/* aligned) with plain streaming loads, so that a caller can time the        */
-/* practical HBM read ceiling that the verification kernel's bandwidth is    */
-/* compared with.  `sink` is a device float that is written only in a        */
-/* pathological case (it keeps the loads alive).  Enqueued on `stream`.      */
+/* aligned) with non-temporal loads in the verification kernel's access      */
+/* pattern (two workgroups per CU, each streaming one contiguous range in    */
+/* 32 KB blocks), so that a caller can time the practical HBM read ceiling   */
+/* that the verification kernel's bandwidth is compared with.  `sink` is a   */
+/* device float that is written only in a pathological case (it keeps the    */
+/* loads alive).  Enqueued on the current device's `stream`.  Errors:        */
+/* DSV_ERR_INVALID_ARG (null, unaligned or shorter than 16 bytes),           */
+/* DSV_ERR_HIP (device query or launch failed).                              */
 /* ------------------------------------------------------------------------ */
 dsv_status dsv_probe_stream_read(const void *buf, size_t bytes, float *sink, hipStream_t stream);
 
