@@ -35,8 +35,8 @@ def test_config1_fp32():
 def test_bf16_ragged(d_head, hq, hkv, kv_chunk):
     if (d_head, hq, hkv) == (256, 4, 4):
         pytest.skip("head_dim 256 with one query head per KV head: a GPU memory fault was seen "
-                    "on the multi-stage schedule for this shape (since switched off for it); "
-                    "the cause is not yet shown, so the case stays off the GPU")
+                    "with an earlier schedule of direct global->LDS loads for this shape (that "
+                    "code is gone); its cause was never shown, so the case stays off the GPU")
     c = small_case(10 + d_head + hq, hq=hq, hkv=hkv, d=d_head,
                    k=(16, 5, 0, 11, 1, 16, 3), ctx=(700, 0, 40, 63, 64, 1000, 129))
     _run(c, kv_chunk=kv_chunk, tag=f"d{d_head} hq{hq} hkv{hkv} chunk{kv_chunk}")
