@@ -8,9 +8,12 @@
 // draft logits is the acceptance signal.
 //
 // Both vocabulary sweeps are HBM-bound streams over fp32 logits.  Each row is cut into
-// chunks so that the launch has thousands of workgroups for 256 CUs; a chunk reduces to one
-// 64-bit key per row (argmax) or one (top-1 key, top-2 value) pair (margin), and a small
-// per-request kernel merges the chunks in a fixed order, so results are deterministic.
+// chunks so that the launch has about 2048 workgroups, each streaming one contiguous chunk
+// in 32 KB blocks (eight 16-byte non-temporal loads in flight per thread, the next block's
+// loads issued before the current block is reduced);
+// a chunk reduces to one 64-bit key per row (argmax) or one (top-1 key, top-2 value) pair
+// (margin), and a small per-request kernel merges the chunks in a fixed order, so results
+// are deterministic.
 //
 // Argmax key: (order-preserving bits of the value) << 32 | ~index.  The largest key has the
 // largest value and, among equal values, the lowest index; -0.0 is folded onto +0.0.  A NaN
@@ -20,6 +23,8 @@
 namespace dsv {
 
 constexpr int kAccThreads = 256;
+constexpr int kAccLoads = 8;                            // 16-byte loads in flight per thread
+constexpr int kAccBlock = kAccThreads * 4 * kAccLoads;  // floats per 32 KB block
 constexpr uint64_t kNanKey = ~0ull;
 
 struct Top2 {
@@ -72,30 +77,47 @@ __global__ __launch_bounds__(kAccThreads) void argmax_partial_kernel(
   bool nan = false;
   const int t = threadIdx.x;
   if (kVec4) {
-    // four independent 16-byte loads in flight per thread
+    // kAccLoads independent 16-byte loads in flight per thread; the next block's loads are
+    // issued before the current block is reduced
     constexpr int64_t kStep = 4 * kAccThreads;
-    for (int64_t v0 = lo + 4 * t; v0 < hi; v0 += 4 * kStep) {
-      float4 f[4];
+    auto load = [&](f32x4 (&f)[kAccLoads], int64_t v0) __attribute__((always_inline)) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kAccLoads; ++u) {
         const int64_t v = v0 + u * kStep;
-        const f32x4 ld = v < hi ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(x + v))
-                                : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-        f[u] = make_float4(ld[0], ld[1], ld[2], ld[3]);
+        f[u] = v < hi ? gload_stream<f32x4>(x + v) : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       }
+    };
+    // A thread visits its elements in increasing index order, so a strict comparison keeps
+    // the lowest index among equal values (and -0.0 == +0.0); the value/index pair becomes a
+    // key only once, for the cross-thread merge.
+    float bv = -INFINITY;
+    int64_t bi = -1;
+    auto reduce = [&](const f32x4 (&f)[kAccLoads], int64_t v0) __attribute__((always_inline)) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kAccLoads; ++u) {
         const int64_t v = v0 + u * kStep;
         if (v >= hi) continue;
-        const float e[4] = {f[u].x, f[u].y, f[u].z, f[u].w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          nan |= e[q] != e[q];
-          uint64_t key = ((uint64_t)ordered_bits(e[q]) << 32) | (uint32_t)~(uint32_t)(v + q);
-          best = key > best ? key : best;
+          const float e = f[u][q];
+          nan |= e != e;
+          const bool gt = e > bv || bi < 0;
+          bv = gt ? e : bv;
+          bi = gt ? v + q : bi;
         }
       }
+    };
+    f32x4 fa[kAccLoads], fb[kAccLoads];
+    int64_t v0 = lo + 4 * t;
+    if (v0 < hi) load(fa, v0);
+    for (; v0 < hi; v0 += 2 * kAccBlock) {
+      if (v0 + kAccBlock < hi) load(fb, v0 + kAccBlock);
+      reduce(fa, v0);
+      if (v0 + kAccBlock >= hi) break;
+      if (v0 + 2 * kAccBlock < hi) load(fa, v0 + 2 * kAccBlock);
+      reduce(fb, v0 + kAccBlock);
     }
+    if (bi >= 0) best = ((uint64_t)ordered_bits(bv) << 32) | (uint32_t)~(uint32_t)bi;
   } else {
     for (int64_t v = lo + t; v < hi; v += kAccThreads) {
       float e = x[v];
@@ -131,23 +153,19 @@ __global__ __launch_bounds__(kAccThreads) void top2_partial_kernel(
   const int t = threadIdx.x;
   if (kVec4) {
     constexpr int64_t kStep = 4 * kAccThreads;
-    for (int64_t v0 = lo + 4 * t; v0 < hi; v0 += 4 * kStep) {
-      float4 f[4];
+    for (int64_t v0 = lo + 4 * t; v0 < hi; v0 += kAccBlock) {
+      f32x4 f[kAccLoads];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kAccLoads; ++u) {
         const int64_t v = v0 + u * kStep;
-        const f32x4 ld = v < hi ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(x + v))
-                                : f32x4{0.f, 0.f, 0.f, 0.f};
-        f[u] = make_float4(ld[0], ld[1], ld[2], ld[3]);
+        f[u] = v < hi ? gload_stream<f32x4>(x + v) : f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kAccLoads; ++u) {
         const int64_t v = v0 + u * kStep;
         if (v >= hi) continue;
-        top2_push(acc, f[u].x, (uint32_t)v);
-        top2_push(acc, f[u].y, (uint32_t)v + 1);
-        top2_push(acc, f[u].z, (uint32_t)v + 2);
-        top2_push(acc, f[u].w, (uint32_t)v + 3);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) top2_push(acc, f[u][q], (uint32_t)(v + q));
       }
     }
   } else {
@@ -269,11 +287,12 @@ __global__ __launch_bounds__(kWave) void accept_finalize_kernel(
   }
 }
 
-// Chunking of a [rows][vocab] sweep: about 2048+ workgroups, chunks of >= 2048 elements,
-// multiples of 1024 (four per lane of a 256-thread workgroup).
+// Chunking of a [rows][vocab] sweep: about 2048 workgroups (eight per CU over the launch), chunks
+// of at least one 32 KB block, multiples of 1024 elements (four per lane of a 256-thread
+// workgroup).
 static void plan_chunks(int64_t rows, int64_t vocab, int *n_chunks, int *chunk) {
   int64_t want = rows > 0 ? (2048 + rows - 1) / rows : 1;
-  int64_t cap = (vocab + 2047) / 2048;
+  int64_t cap = (vocab + kAccBlock - 1) / kAccBlock;
   if (cap < 1) cap = 1;
   int64_t n = want < 1 ? 1 : (want > cap ? cap : want);
   int64_t c = (vocab + n - 1) / n;
