@@ -82,6 +82,7 @@ def _load():
         lib.oracle_accept.argtypes = [i32, i32, i32] + [P] * 8
         lib.oracle_top2_margin.argtypes = [i64, i64, P, P, P]
         lib.oracle_threads.argtypes = []
+        lib.oracle_allocate.argtypes = [i32, i32, i32, i32, P, P, P]
         _lib = lib
     return _lib
 
@@ -138,6 +139,29 @@ def pack(k, ctx_len, kv_base, block_tokens, W: int, m_bs: int) -> dict:
             _p(out["slot_cache_loc"]),
         )
     )
+    return out
+
+
+# --------------------------------------------------------------------------
+# Budget allocator
+# --------------------------------------------------------------------------
+def allocate(scores, n_live: int, W: int, m_live: int) -> dict:
+    """Seeded lengths k0 and adjusted lengths k ([n_bs] int32) from draft scores [n_bs, W-1]
+    (rows >= n_live are inactive).  DScale Sec. III-C, Budget allocator."""
+    lib = _load()
+    scores = _c(scores, np.float32)
+    n_bs = scores.shape[0]
+    scores = scores.reshape(n_bs, W - 1) if n_bs else scores.reshape(0, max(W - 1, 0))
+    out = dict(k0=np.zeros(n_bs, np.int32), k=np.zeros(n_bs, np.int32))
+    _check(lib.oracle_allocate(n_live, n_bs, W, m_live, _p(scores), _p(out["k0"]), _p(out["k"])))
+    return out
+
+
+def allocate_pack(scores, n_live: int, W: int, m_live: int, m_bs: int, ctx_len, kv_base, block_tokens) -> dict:
+    """Budget allocator followed by the flat-buffer packer on the adjusted lengths."""
+    a = allocate(scores, n_live, W, m_live)
+    out = pack(a["k"], ctx_len, kv_base, block_tokens, W, m_bs)
+    out.update(a)
     return out
 
 

@@ -97,6 +97,70 @@ int oracle_pack(int n_bs, int W, int m_bs, const int32_t *k, const int32_t *ctx_
 }
 
 /* ------------------------------------------------------------------------ */
+/* Budget allocator (DScale Sec. III-C, "Acceptance predictor" and "Budget   */
+/* allocator", Algorithm 1 steps from the sigmoid scores on, Fig. 6).        */
+/*                                                                            */
+/* Input: per live request i < n_live, W - 1 draft acceptance scores         */
+/* (sigmoid outputs of the predictor; the predictor itself needs trained     */
+/* weights and is not part of this function).                               */
+/*   prefix scores: q[i][0] = 1 (the known anchor), q[i][j] = min(q[i][j-1], */
+/*     score[i][j-1]) -- acceptance needs accepted predecessors;             */
+/*   estimate: l_i = q[i][1] + ... + q[i][W-1] (fp32, added in that order);  */
+/*   seed: k0_i = l_i rounded to nearest (ties to even), clipped to [1, W];  */
+/*   gap: delta = m_live - sum_i k0_i;                                       */
+/*   while delta > 0: the request with the largest next-slot score           */
+/*     q[i][k_i] (k_i < W; ties: lowest i) grows by one;                     */
+/*   while delta < 0: the request with the smallest last-slot score          */
+/*     q[i][k_i - 1] (k_i > 1, the anchor stays; ties: lowest i) shrinks.    */
+/* Requests n_live .. n_bs - 1 are inactive: k = 0.  A NaN score counts as   */
+/* 0.  If no request can move, the loop stops (the caller sees sum k !=     */
+/* m_live).  Writes k[n_bs] and k0[n_bs]; returns OR_ERR_ARG on bad sizes.   */
+/* ------------------------------------------------------------------------ */
+int oracle_allocate(int n_live, int n_bs, int W, int m_live, const float *score, int32_t *k0,
+                    int32_t *k) {
+  if (n_live < 0 || n_bs < n_live || W < 1 || W > 64 || m_live < 0) return OR_ERR_ARG;
+  float *q = (float *)malloc(sizeof(float) * (size_t)(n_live > 0 ? n_live : 1) * (size_t)W);
+  if (!q) return OR_ERR_ARG;
+  int64_t total = 0;
+  for (int i = 0; i < n_live; ++i) {
+    float *qi = q + (size_t)i * W;
+    qi[0] = 1.0f;
+    float l = 0.0f;
+    for (int j = 1; j < W; ++j) {
+      float x = score[(size_t)i * (W - 1) + (j - 1)];
+      if (x != x) x = 0.0f;
+      qi[j] = x < qi[j - 1] ? x : qi[j - 1];
+      l = l + qi[j];
+    }
+    float r = rintf(l);
+    int ki = r < 1.0f ? 1 : (r > (float)W ? W : (int)r);
+    k0[i] = ki;
+    k[i] = ki;
+    total += ki;
+  }
+  for (int i = n_live; i < n_bs; ++i) k0[i] = k[i] = 0;
+  int64_t delta = (int64_t)m_live - total;
+  while (delta > 0) {
+    int best = -1;
+    for (int i = 0; i < n_live; ++i)
+      if (k[i] < W && (best < 0 || q[(size_t)i * W + k[i]] > q[(size_t)best * W + k[best]])) best = i;
+    if (best < 0) break;
+    k[best] += 1;
+    delta -= 1;
+  }
+  while (delta < 0) {
+    int best = -1;
+    for (int i = 0; i < n_live; ++i)
+      if (k[i] > 1 && (best < 0 || q[(size_t)i * W + k[i] - 1] < q[(size_t)best * W + k[best] - 1])) best = i;
+    if (best < 0) break;
+    k[best] -= 1;
+    delta += 1;
+  }
+  free(q);
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Attention for one query row: keys/values are the first n rows of K and V */
 /* (row-major [n, d], already in double).                                    */
 /*   z_p = scale * sum_c q_c K[p][c];  m = max_p z_p;  w_p = exp(z_p - m);   */
