@@ -12,6 +12,7 @@ from ._lib import DsvError, MAX_W, STATUS_BAD_REQUEST, STATUS_BUDGET, STATUS_NAN
 from .api import (
     Prefill,
     accept,
+    allocate_pack,
     accept_workspace_bytes,
     attn_args,
     new_status,
@@ -23,7 +24,7 @@ from .api import (
 
 __all__ = [
     "DsvError", "MAX_W", "STATUS_BAD_REQUEST", "STATUS_BUDGET", "STATUS_NAN", "STATUS_POOL",
-    "STATUS_PREFILL", "Prefill", "accept", "accept_workspace_bytes", "attn_args", "new_status",
+    "STATUS_PREFILL", "Prefill", "accept", "accept_workspace_bytes", "allocate_pack", "attn_args", "new_status",
     "pack_slots", "verify_attn", "verify_attn_call", "verify_attn_workspace_bytes",
 ]
 

@@ -71,6 +71,8 @@ def load():
     lib.dsv_attn_args_size.restype = ctypes.c_size_t
     lib.dsv_pack_slots.argtypes = [i32, i32, i32] + [P] * 10 + [P]
     lib.dsv_pack_slots.restype = ctypes.c_int
+    lib.dsv_allocate_pack.argtypes = [i32] * 5 + [P] * 12 + [P]
+    lib.dsv_allocate_pack.restype = ctypes.c_int
     lib.dsv_verify_attn_workspace_bytes.argtypes = [ctypes.POINTER(AttnArgs)]
     lib.dsv_verify_attn_workspace_bytes.restype = ctypes.c_size_t
     lib.dsv_verify_attn.argtypes = [ctypes.POINTER(AttnArgs), P]

@@ -63,6 +63,37 @@ def pack_slots(k, ctx_len, kv_base, block_tokens, m_bs: int, status, out=None, s
     return out
 
 
+def allocate_pack(scores, n_live: int, m_live: int, ctx_len, kv_base, block_tokens, m_bs: int, status,
+                  out=None, stream=None) -> dict:
+    """Budget allocator fused with the packer: draft scores [n_bs, W-1] fp32 -> adjusted
+    lengths k, seeds k0, offsets and slot arrays (device tensors; `out` may supply them)."""
+    lib = _lib.load()
+    dev = ctx_len.device
+    n_bs, W = block_tokens.shape
+    _need(scores, torch.float32, "scores", dev)
+    if tuple(scores.shape) != (n_bs, W - 1):
+        raise ValueError(f"scores must be [{n_bs}, {W - 1}], got {tuple(scores.shape)}")
+    for t, dt, nm in ((ctx_len, torch.int32, "ctx_len"), (kv_base, torch.int64, "kv_base"),
+                      (block_tokens, torch.int32, "block_tokens")):
+        _need(t, dt, nm, dev)
+    if out is None:
+        out = dict(
+            k=torch.empty(n_bs, dtype=torch.int32, device=dev),
+            k0=torch.empty(n_bs, dtype=torch.int32, device=dev),
+            offsets=torch.empty(n_bs + 1, dtype=torch.int32, device=dev),
+            slot_req=torch.empty(m_bs, dtype=torch.int32, device=dev),
+            slot_tok=torch.empty(m_bs, dtype=torch.int32, device=dev),
+            slot_pos=torch.empty(m_bs, dtype=torch.int32, device=dev),
+            slot_cache_loc=torch.empty(m_bs, dtype=torch.int64, device=dev),
+        )
+    check(lib.dsv_allocate_pack(n_live, n_bs, W, m_live, m_bs, _ptr(scores), _ptr(ctx_len), _ptr(kv_base),
+                                _ptr(block_tokens), _ptr(out["k"]), _ptr(out.get("k0")), _ptr(out["offsets"]),
+                                _ptr(out["slot_req"]), _ptr(out["slot_tok"]), _ptr(out["slot_pos"]),
+                                _ptr(out["slot_cache_loc"]), _ptr(status), _stream(stream)),
+          "dsv_allocate_pack")
+    return out
+
+
 # ---------------------------------------------------------------------------
 # dsv_verify_attn
 # ---------------------------------------------------------------------------

@@ -91,6 +91,168 @@ __global__ __launch_bounds__(kPackMaxThreads) void pack_slots_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Budget allocator fused with the packer (DScale Sec. III-C, "Acceptance predictor" from
+// the sigmoid scores on, "Budget allocator", Fig. 6).  One workgroup, one thread per
+// request (n_bs <= 1024), no host round trip.
+//
+// The pages adjust the seeded lengths one slot at a time: grow the request whose next slot
+// has the highest score, or shrink the one whose last slot has the lowest score, until the
+// live budget is met.  Because every request's prefix scores are nonincreasing, the |delta|
+// slots that loop moves are exactly the |delta| largest candidates under the order (score
+// desc, request asc, slot asc) when growing -- candidates are the slots j in [k0_i, W) -- or
+// the smallest under (score asc, request asc, slot desc) when shrinking (slots j in
+// [1, k0_i)).  The kernel selects them directly: a 32-step bisection on the order-preserving
+// score bits finds the score of the last moved slot, every slot beyond it moves, and the
+// slots equal to it move in request order (an exclusive scan).  Same result as the loop;
+// 32 block-wide counts instead of up to 7N sequential arg-max steps.
+// ---------------------------------------------------------------------------
+constexpr int kAllocMaxRequests = 1024;
+
+__device__ __forceinline__ int block_sum_i32(int v, int *red, int lane, int wv, int nwv) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  __syncthreads();  // previous readers of red[] are done
+  if (lane == 0) red[wv] = v;
+  __syncthreads();
+  int t = 0;
+  for (int w = 0; w < nwv; ++w) t += red[w];
+  return t;
+}
+
+// Exclusive scan of v over the workgroup's threads in order; *total receives the sum.
+__device__ __forceinline__ int block_exclusive_scan_i32(int v, int *red, int lane, int wv, int nwv,
+                                                        int *total) {
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  __syncthreads();
+  if (lane == kWave - 1) red[wv] = incl;
+  __syncthreads();
+  int before = 0, t = 0;
+  for (int w = 0; w < nwv; ++w) {
+    before += w < wv ? red[w] : 0;
+    t += red[w];
+  }
+  *total = t;
+  return before + incl - v;
+}
+
+__global__ __launch_bounds__(kAllocMaxRequests) void allocate_pack_kernel(
+    int n_live, int n_bs, int W, int m_live, int m_bs, const float *__restrict__ score,
+    const int32_t *__restrict__ ctx_len, const int64_t *__restrict__ kv_base,
+    const int32_t *__restrict__ block_tokens, int32_t *__restrict__ k_out, int32_t *__restrict__ k0_out,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ slot_req, int32_t *__restrict__ slot_tok,
+    int32_t *__restrict__ slot_pos, int64_t *__restrict__ slot_cache_loc, int32_t *status) {
+  __shared__ int red[kAllocMaxRequests / kWave];
+  const int i = threadIdx.x, lane = i & (kWave - 1), wv = i / kWave, nwv = blockDim.x / kWave;
+  const bool live = i < n_live;
+
+  // prefix scores (q[0] = 1 for the anchor, cumulative minimum after) and the rounded seed
+  uint32_t u[DSV_MAX_W];  // order-preserving bits of q[j]
+  int k0 = 0;
+  if (live) {
+    float prev = 1.0f, l = 0.0f;
+    bool nan = false;
+    u[0] = ordered_bits(1.0f);
+#pragma unroll
+    for (int j = 1; j < DSV_MAX_W; ++j) {
+      if (j < W) {
+        float x = score[(int64_t)i * (W - 1) + (j - 1)];
+        nan |= x != x;
+        x = x != x ? 0.0f : x;
+        prev = x < prev ? x : prev;
+        l = l + prev;
+        u[j] = ordered_bits(prev);
+      }
+    }
+    if (nan) status_or(status, DSV_STATUS_NAN);
+    const float r = rintf(l);
+    k0 = r < 1.0f ? 1 : (r > (float)W ? W : (int)r);
+  }
+  const int total0 = block_sum_i32(k0, red, lane, wv, nwv);
+  const int delta = m_live - total0;  // uniform
+  int k = k0;
+  if (delta != 0 && n_live > 0) {
+    const bool grow = delta > 0;
+    // candidate j of this request: growing j in [k0, W) with key u[j]; shrinking j in
+    // [1, k0) with key ~u[j] (larger key = moved earlier)
+    const int jlo = grow ? k0 : 1, jhi = grow ? W : k0;
+    auto key = [&](int j) __attribute__((always_inline)) { return grow ? u[j] : ~u[j]; };
+    auto count_ge = [&](uint32_t t) __attribute__((always_inline)) {
+      int c = 0;
+      if (live) {
+#pragma unroll
+        for (int j = 0; j < DSV_MAX_W; ++j) c += (j >= jlo && j < jhi && key(j) >= t) ? 1 : 0;
+      }
+      return c;
+    };
+    int want = grow ? delta : -delta;
+    const int avail = block_sum_i32(live ? (jhi > jlo ? jhi - jlo : 0) : 0, red, lane, wv, nwv);
+    want = want < avail ? want : avail;  // if nobody can move further, move everything
+    int moved = 0;
+    if (want > 0) {
+      // largest threshold T with count(key >= T) >= want
+      uint32_t T = 0;
+      for (int b = 31; b >= 0; --b) {
+        const uint32_t t = T | (1u << b);
+        if (block_sum_i32(count_ge(t), red, lane, wv, nwv) >= want) T = t;
+      }
+      int gt = 0, eq = 0;
+      if (live) {
+#pragma unroll
+        for (int j = 0; j < DSV_MAX_W; ++j) {
+          const bool in = j >= jlo && j < jhi;
+          gt += (in && key(j) > T) ? 1 : 0;
+          eq += (in && key(j) == T) ? 1 : 0;
+        }
+      }
+      const int n_gt = block_sum_i32(gt, red, lane, wv, nwv);
+      int eq_total;
+      const int eq_before = block_exclusive_scan_i32(eq, red, lane, wv, nwv, &eq_total);
+      int take = want - n_gt - eq_before;
+      take = take < 0 ? 0 : (take > eq ? eq : take);
+      moved = gt + take;
+    }
+    k = grow ? k0 + moved : k0 - moved;
+  }
+
+  // flat-buffer pack of the adjusted lengths
+  int end;
+  const int off = block_exclusive_scan_i32(k, red, lane, wv, nwv, &end);
+  if (end > m_bs) {  // cannot happen for m_live <= m_bs; kept as the packer's rule
+    if (i == 0) status_or(status, DSV_STATUS_BUDGET);
+  }
+  const bool fits = end <= m_bs;
+  if (i < n_bs) {
+    k_out[i] = k;
+    if (k0_out) k0_out[i] = k0;
+    offsets[i] = fits ? off : 0;
+    if (fits) {
+      const int c = ctx_len[i];
+      const int64_t kb = kv_base[i];
+      for (int j = 0; j < k; ++j) {
+        const int s = off + j;
+        slot_req[s] = i;
+        slot_tok[s] = block_tokens[(int64_t)i * W + j];
+        slot_pos[s] = c + j;
+        slot_cache_loc[s] = kb + c + j;
+      }
+    }
+  }
+  const int tail = fits ? end : 0;
+  if (i == 0) offsets[n_bs] = tail;
+  for (int s = tail + i; s < m_bs; s += blockDim.x) {
+    slot_req[s] = -1;
+    slot_tok[s] = 0;
+    slot_pos[s] = 0;
+    slot_cache_loc[s] = -1;
+  }
+}
+
 }  // namespace dsv
 
 extern "C" dsv_status dsv_pack_slots(int32_t n_bs, int32_t W, int32_t m_bs, const int32_t *k,
@@ -110,6 +272,28 @@ extern "C" dsv_status dsv_pack_slots(int32_t n_bs, int32_t W, int32_t m_bs, cons
   hipLaunchKernelGGL(dsv::pack_slots_kernel, dim3(1), dim3(nt), 0, stream, n_bs, W,
                      m_bs, k, ctx_len, kv_base, block_tokens, offsets, slot_req, slot_tok, slot_pos,
                      slot_cache_loc, status);
+  DSV_LAUNCH_CHECK();
+  return DSV_OK;
+}
+
+extern "C" dsv_status dsv_allocate_pack(int32_t n_live, int32_t n_bs, int32_t W, int32_t m_live,
+                                        int32_t m_bs, const float *scores, const int32_t *ctx_len,
+                                        const int64_t *kv_base, const int32_t *block_tokens,
+                                        int32_t *k, int32_t *k0, int32_t *offsets, int32_t *slot_req,
+                                        int32_t *slot_tok, int32_t *slot_pos, int64_t *slot_cache_loc,
+                                        int32_t *status, hipStream_t stream) {
+  if (n_live < 0 || n_bs < n_live || n_bs > dsv::kAllocMaxRequests || W < 1 || W > DSV_MAX_W ||
+      m_live < 0 || m_bs < m_live)
+    return DSV_ERR_INVALID_ARG;
+  if (!k || !offsets || !status) return DSV_ERR_INVALID_ARG;
+  if (n_live > 0 && W > 1 && !scores) return DSV_ERR_INVALID_ARG;
+  if (n_bs > 0 && (!ctx_len || !kv_base || !block_tokens)) return DSV_ERR_INVALID_ARG;
+  if (m_bs > 0 && (!slot_req || !slot_tok || !slot_pos || !slot_cache_loc)) return DSV_ERR_INVALID_ARG;
+  int want = n_bs > 64 ? n_bs : 64;
+  const int nt = (want + 63) / 64 * 64;
+  hipLaunchKernelGGL(dsv::allocate_pack_kernel, dim3(1), dim3(nt), 0, stream, n_live, n_bs, W, m_live,
+                     m_bs, scores, ctx_len, kv_base, block_tokens, k, k0, offsets, slot_req, slot_tok,
+                     slot_pos, slot_cache_loc, status);
   DSV_LAUNCH_CHECK();
   return DSV_OK;
 }

@@ -106,6 +106,41 @@ dsv_status dsv_pack_slots(int32_t n_bs, int32_t W, int32_t m_bs, const int32_t *
                           int32_t *status, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* dsv_allocate_pack -- budget allocator fused with the flat-buffer packer   */
+/*                                                                            */
+/* DScale Sec. III-C ("Acceptance predictor" from the sigmoid scores on,     */
+/* "Budget allocator", "Flat-buffer packer", Fig. 6).  For each live request */
+/* i < n_live, scores[i][0 .. W-2] are the acceptance scores of draft        */
+/* positions 1 .. W-1 (sigmoid outputs of a predictor, which is not part of  */
+/* the library).  Prefix scores: q[i][0] = 1 (anchor), q[i][j] =             */
+/* min(q[i][j-1], scores[i][j-1]); a NaN score counts as 0 and sets          */
+/* DSV_STATUS_NAN.  Seed: k0_i = the fp32 sum q[i][1] + ... + q[i][W-1]      */
+/* (added in that order) rounded to nearest, ties to even, clipped to        */
+/* [1, W].  The seeds are then adjusted until sum k = m_live: slots are      */
+/* added, one at a time, to the request whose next slot q[i][k_i] scores     */
+/* highest, or removed from the request whose last slot q[i][k_i - 1]        */
+/* scores lowest (the anchor is never removed; k_i <= W; ties go to the      */
+/* lowest request index).  If every request reaches W (or 1) first, the      */
+/* adjustment stops there.  Requests n_live .. n_bs-1 get k = 0.  The        */
+/* adjusted lengths are then packed exactly as by dsv_pack_slots.            */
+/*                                                                            */
+/* Inputs  scores[n_bs][W-1] fp32 (rows >= n_live unread), ctx_len, kv_base, */
+/*         block_tokens as for dsv_pack_slots.                               */
+/* Outputs k[n_bs] adjusted lengths, k0[n_bs] seeds (nullable), offsets and  */
+/*         slot arrays as for dsv_pack_slots.                                */
+/* Sizes   0 <= n_live <= n_bs <= 1024, 1 <= W <= DSV_MAX_W,                 */
+/*         0 <= m_live <= m_bs.                                              */
+/* Errors  host: DSV_ERR_INVALID_ARG for sizes outside these bounds or a     */
+/*         missing pointer; device: DSV_STATUS_NAN as above.                 */
+/* One kernel launch (a single workgroup), no host synchronisation.         */
+/* ------------------------------------------------------------------------ */
+dsv_status dsv_allocate_pack(int32_t n_live, int32_t n_bs, int32_t W, int32_t m_live, int32_t m_bs,
+                             const float *scores, const int32_t *ctx_len, const int64_t *kv_base,
+                             const int32_t *block_tokens, int32_t *k, int32_t *k0, int32_t *offsets,
+                             int32_t *slot_req, int32_t *slot_tok, int32_t *slot_pos,
+                             int64_t *slot_cache_loc, int32_t *status, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* dsv_verify_attn -- tile-routed attention over packed slots                */
 /*                                                                            */
 /* DScale Sec. III-B (Path-aware tile router: verification rows, at most     */
