@@ -88,6 +88,55 @@ def kv_bytes(ctx_len, k, hkv, d, elem=2):
     return int(sum((int(c) + int(kk)) * hkv * d * 2 * elem for c, kk in zip(ctx_len, k)))
 
 
+def time_allocator(dev, iters: int = 50):
+    """Latency of the budget allocator fused with the packer (dsv_allocate_pack) next to the
+    plain packer, at the request counts of the 8-request and 60-request verification sets
+    (W = 16, live budget 8 N in a bucket of 8 n_bs slots), with seeded synthetic scores.  Both
+    are single-workgroup launches; reported as device microseconds per call, from HIP-graph
+    replays of back-to-back calls timed with HIP events."""
+    import numpy as np
+    import torch
+    import block_verification_attention_amd as dsv
+    out = {}
+    for n_live, n_bs in ((8, 8), (60, 64)):
+        rng = np.random.default_rng(5000 + n_live)
+        scores = torch.from_numpy(rng.random((n_bs, 15), dtype=np.float32)).to(dev)
+        ctx = torch.from_numpy(rng.integers(0, 8192, n_bs).astype(np.int32)).to(dev)
+        base = torch.from_numpy(np.arange(n_bs, dtype=np.int64) * 40000).to(dev)
+        toks = torch.from_numpy(rng.integers(0, 150000, (n_bs, 16)).astype(np.int32)).to(dev)
+        k = torch.from_numpy(np.minimum(rng.integers(1, 17, n_bs), 16).astype(np.int32)).to(dev)
+        st = dsv.new_status(dev)
+        alloc = dsv.allocate_pack(scores, n_live, 8 * n_live, ctx, base, toks, 8 * n_bs, st)
+        packed = dsv.pack_slots(k, ctx, base, toks, 16 * n_bs, st)
+        res = {}
+        for name, fn in (("allocate_pack_us", lambda: dsv.allocate_pack(scores, n_live, 8 * n_live, ctx, base, toks,
+                                                                        8 * n_bs, st, out=alloc)),
+                         ("pack_only_us", lambda: dsv.pack_slots(k, ctx, base, toks, 16 * n_bs, st, out=packed))):
+            # `iters` back-to-back calls captured in one HIP graph, so that the host's launch
+            # latency does not separate them; device time per call
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                for _ in range(3):
+                    fn()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=s):
+                    for _ in range(iters):
+                        fn()
+            torch.cuda.current_stream().wait_stream(s)
+            g.replay()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(5):
+                g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            res[name] = a.elapsed_time(b) * 1e3 / (5 * iters)
+        res["budget_met"] = int(alloc["k"].sum().item()) == 8 * n_live
+        out[f"n_live_{n_live}"] = res
+    return out
+
+
 def cpu_baseline(case, n_req_sample: int):
     """The oracle (pack + fp64 attention + greedy accept) on the first n_req_sample requests."""
     import numpy as np
@@ -294,6 +343,7 @@ def main():
     pool_bytes = 2 * kp0.numel() * 2
     res["roofline"]["stream_read_ceiling_GBs"] = pool_bytes / (probe_avg * 1e-3) / 1e9
     res["roofline"]["frac_of_ceiling"] = achieved / res["roofline"]["stream_read_ceiling_GBs"]
+    res["allocator"] = time_allocator(dev)
     if args.cpu_sample > 0:
         res["cpu_baseline"] = cpu_baseline(c, args.cpu_sample)
     print(json.dumps(res))

@@ -109,36 +109,49 @@ __global__ __launch_bounds__(kPackMaxThreads) void pack_slots_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kAllocMaxRequests = 1024;
 
-__device__ __forceinline__ int block_sum_i32(int v, int *red, int lane, int wv, int nwv) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  __syncthreads();  // previous readers of red[] are done
-  if (lane == 0) red[wv] = v;
-  __syncthreads();
+// Sum over the workgroup of small per-thread counts 0 <= v < 32: within a wavefront from
+// five ballots (bit b of every lane's count, population-counted), no cross-lane data
+// movement; across wavefronts through LDS (a one-wavefront workgroup needs no barrier).
+__device__ __forceinline__ int block_sum_small(int v, int *red, int lane, int wv, int nwv) {
   int t = 0;
-  for (int w = 0; w < nwv; ++w) t += red[w];
-  return t;
+#pragma unroll
+  for (int b = 0; b < 5; ++b) t += __popcll(__ballot((v >> b) & 1)) << b;
+  if (nwv == 1) return t;
+  __syncthreads();  // previous readers of red[] are done
+  if (lane == 0) red[wv] = t;
+  __syncthreads();
+  int s = 0;
+  for (int w = 0; w < nwv; ++w) s += red[w];
+  return s;
 }
 
-// Exclusive scan of v over the workgroup's threads in order; *total receives the sum.
-__device__ __forceinline__ int block_exclusive_scan_i32(int v, int *red, int lane, int wv, int nwv,
-                                                        int *total) {
-  int incl = v;
+// Exclusive scan of small counts 0 <= v < 32 over the workgroup's threads in order (ballots
+// masked to the lower lanes within a wavefront, LDS across wavefronts); *total receives the
+// sum.
+__device__ __forceinline__ int block_exclusive_scan_small(int v, int *red, int lane, int wv, int nwv,
+                                                          int *total) {
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  int pre = 0, t = 0;
 #pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int o = __shfl_up(incl, d);
-    if (lane >= d) incl += o;
+  for (int b = 0; b < 5; ++b) {
+    const uint64_t m = __ballot((v >> b) & 1);
+    pre += __popcll(m & below) << b;
+    t += __popcll(m) << b;
+  }
+  if (nwv == 1) {
+    *total = t;
+    return pre;
   }
   __syncthreads();
-  if (lane == kWave - 1) red[wv] = incl;
+  if (lane == 0) red[wv] = t;
   __syncthreads();
-  int before = 0, t = 0;
+  int before = 0, all = 0;
   for (int w = 0; w < nwv; ++w) {
     before += w < wv ? red[w] : 0;
-    t += red[w];
+    all += red[w];
   }
-  *total = t;
-  return before + incl - v;
+  *total = all;
+  return before + pre;
 }
 
 __global__ __launch_bounds__(kAllocMaxRequests) void allocate_pack_kernel(
@@ -173,7 +186,7 @@ __global__ __launch_bounds__(kAllocMaxRequests) void allocate_pack_kernel(
     const float r = rintf(l);
     k0 = r < 1.0f ? 1 : (r > (float)W ? W : (int)r);
   }
-  const int total0 = block_sum_i32(k0, red, lane, wv, nwv);
+  const int total0 = block_sum_small(k0, red, lane, wv, nwv);
   const int delta = m_live - total0;  // uniform
   int k = k0;
   if (delta != 0 && n_live > 0) {
@@ -191,7 +204,7 @@ __global__ __launch_bounds__(kAllocMaxRequests) void allocate_pack_kernel(
       return c;
     };
     int want = grow ? delta : -delta;
-    const int avail = block_sum_i32(live ? (jhi > jlo ? jhi - jlo : 0) : 0, red, lane, wv, nwv);
+    const int avail = block_sum_small(live ? (jhi > jlo ? jhi - jlo : 0) : 0, red, lane, wv, nwv);
     want = want < avail ? want : avail;  // if nobody can move further, move everything
     int moved = 0;
     if (want > 0) {
@@ -199,7 +212,7 @@ __global__ __launch_bounds__(kAllocMaxRequests) void allocate_pack_kernel(
       uint32_t T = 0;
       for (int b = 31; b >= 0; --b) {
         const uint32_t t = T | (1u << b);
-        if (block_sum_i32(count_ge(t), red, lane, wv, nwv) >= want) T = t;
+        if (block_sum_small(count_ge(t), red, lane, wv, nwv) >= want) T = t;
       }
       int gt = 0, eq = 0;
       if (live) {
@@ -210,9 +223,9 @@ __global__ __launch_bounds__(kAllocMaxRequests) void allocate_pack_kernel(
           eq += (in && key(j) == T) ? 1 : 0;
         }
       }
-      const int n_gt = block_sum_i32(gt, red, lane, wv, nwv);
+      const int n_gt = block_sum_small(gt, red, lane, wv, nwv);
       int eq_total;
-      const int eq_before = block_exclusive_scan_i32(eq, red, lane, wv, nwv, &eq_total);
+      const int eq_before = block_exclusive_scan_small(eq, red, lane, wv, nwv, &eq_total);
       int take = want - n_gt - eq_before;
       take = take < 0 ? 0 : (take > eq ? eq : take);
       moved = gt + take;
@@ -222,7 +235,7 @@ __global__ __launch_bounds__(kAllocMaxRequests) void allocate_pack_kernel(
 
   // flat-buffer pack of the adjusted lengths
   int end;
-  const int off = block_exclusive_scan_i32(k, red, lane, wv, nwv, &end);
+  const int off = block_exclusive_scan_small(k, red, lane, wv, nwv, &end);
   if (end > m_bs) {  // cannot happen for m_live <= m_bs; kept as the packer's rule
     if (i == 0) status_or(status, DSV_STATUS_BUDGET);
   }
