@@ -73,7 +73,7 @@ def _load():
         P = ctypes.c_void_p
         i32, i64, dbl = ctypes.c_int, ctypes.c_int64, ctypes.c_double
         lib.oracle_pack.argtypes = [i32, i32, i32] + [P] * 9
-        lib.oracle_verify_attn.argtypes = [i32, i32, i32, i32, dbl, P, P, i64, i64, i64, i32, i32] + [P] * 10
+        lib.oracle_verify_attn.argtypes = [i32, i32, i32, i32, dbl, P, P, i64, i64, i64, i32, i32] + [P] * 5 + [i64] + [P] * 6
         lib.oracle_attn_one_request.argtypes = [i32, i32, i32, i32, dbl, i32, i32, i64] + [P] * 5
         lib.oracle_attn_padded_masked.argtypes = [i32, i32, i32, i32, i32, i32, dbl, i64] + [P] * 6
         lib.oracle_softmax_probs.argtypes = [i32, i32, dbl, P, P, i64, P]
@@ -173,8 +173,10 @@ def _scale(d, scale):
 
 
 def verify_attn(q, k_pool, v_pool, offsets, k, ctx_len, kv_base, k_new=None, v_new=None,
-                scale=0.0, slot_mask=None):
+                scale=0.0, slot_mask=None, kv_index=None):
     """Packed attention.  q [m_bs, hq, d]; pools [hkv, rows, d]; returns (out, lse) in float64.
+    kv_index [n_bs, stride] int32, if given, maps position p of request i to pool row
+    kv_index[i, p] (token-granular cache map) instead of kv_base[i] + p.
 
     Rows that no request owns and that precede offsets[-1] come back as NaN (not written)."""
     lib = _load()
@@ -196,13 +198,18 @@ def verify_attn(q, k_pool, v_pool, offsets, k, ctx_len, kv_base, k_new=None, v_n
         assert k_new.shape == (m_bs, hkv, d) and v_new.shape == (m_bs, hkv, d)
     if slot_mask is not None:
         slot_mask = _c(slot_mask, np.uint8)
+    stride = 0
+    if kv_index is not None:
+        kv_index = _c(kv_index, np.int32)
+        assert kv_index.ndim == 2 and kv_index.shape[0] == n_bs
+        stride = kv_index.shape[1]
     out = np.full((m_bs, hq, d), np.nan)
     lse = np.full((m_bs, hq), np.nan)
     _check(
         lib.oracle_verify_attn(
             dt, hq, hkv, d, _scale(d, scale), _p(k_pool), _p(v_pool), rows, rows * d, d,
-            n_bs, m_bs, _p(offsets), _p(k), _p(ctx_len), _p(kv_base), _p(q), _p(k_new), _p(v_new),
-            _p(slot_mask), _p(out), _p(lse),
+            n_bs, m_bs, _p(offsets), _p(k), _p(ctx_len), _p(kv_base), _p(kv_index), stride, _p(q),
+            _p(k_new), _p(v_new), _p(slot_mask), _p(out), _p(lse),
         )
     )
     return out, lse

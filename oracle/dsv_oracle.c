@@ -208,10 +208,19 @@ static void attend_row(int d, double scale, const double *q, const double *K, co
 /* out 0, lse -inf.  Other rows not owned by any request are not written.    */
 /* slot_mask (nullable, [m_bs]) restricts the computed slots (sampling).     */
 /* ------------------------------------------------------------------------ */
+/* Pool row of position p of request i: the contiguous segment kv_base_i + p, or, with a     */
+/* token-granular cache map (the pages' cacheMap/historyKV gather, Sec. III-D), the row       */
+/* kv_index[i * kv_index_stride + p].                                                          */
+static int64_t pool_row(const int64_t *kv_base, const int32_t *kv_index, int64_t kv_index_stride,
+                        int i, int64_t p) {
+  return kv_index ? (int64_t)kv_index[(int64_t)i * kv_index_stride + p] : kv_base[i] + p;
+}
+
 int oracle_verify_attn(int dtype, int hq, int hkv, int d, double scale, const void *k_pool,
                        const void *v_pool, int64_t pool_rows, int64_t stride_head,
                        int64_t stride_row, int n_bs, int m_bs, const int32_t *offsets,
                        const int32_t *k, const int32_t *ctx_len, const int64_t *kv_base,
+                       const int32_t *kv_index, int64_t kv_index_stride,
                        const void *q, const void *k_new, const void *v_new,
                        const uint8_t *slot_mask, double *out, double *lse) {
   if (hkv <= 0 || hq % hkv != 0 || d <= 0 || n_bs < 0) return OR_ERR_ARG;
@@ -219,7 +228,17 @@ int oracle_verify_attn(int dtype, int hq, int hkv, int d, double scale, const vo
   for (int i = 0; i < n_bs; ++i) {
     if (k[i] < 0 || ctx_len[i] < 0 || kv_base[i] < 0) return OR_ERR_K;
     if (offsets[i] < 0 || offsets[i] + k[i] > m_bs) return OR_ERR_K;
-    if (kv_base[i] + ctx_len[i] + k[i] > pool_rows) return OR_ERR_POOL;
+    if (kv_index) {
+      if ((int64_t)ctx_len[i] + k[i] > kv_index_stride) return OR_ERR_K;
+      /* rows read from the pool: the context, and the candidates when k_new is absent */
+      int64_t n_read = (int64_t)ctx_len[i] + (k_new ? 0 : k[i]);
+      for (int64_t p = 0; p < n_read; ++p) {
+        int64_t r = pool_row(kv_base, kv_index, kv_index_stride, i, p);
+        if (r < 0 || r >= pool_rows) return OR_ERR_POOL;
+      }
+    } else if (kv_base[i] + ctx_len[i] + k[i] > pool_rows) {
+      return OR_ERR_POOL;
+    }
   }
   int end = offsets[n_bs];
   if (end < 0 || end > m_bs) return OR_ERR_ARG;
@@ -253,7 +272,7 @@ int oracle_verify_attn(int dtype, int hq, int hkv, int d, double scale, const vo
           K[p * d + c] = elem(k_new, dtype, (s * hkv + g) * d + c);
           V[p * d + c] = elem(v_new, dtype, (s * hkv + g) * d + c);
         } else {
-          int64_t idx = g * stride_head + (kv_base[i] + p) * stride_row + c;
+          int64_t idx = g * stride_head + pool_row(kv_base, kv_index, kv_index_stride, i, p) * stride_row + c;
           K[p * d + c] = elem(k_pool, dtype, idx);
           V[p * d + c] = elem(v_pool, dtype, idx);
         }

@@ -224,3 +224,80 @@ def test_errors():
     bad[-1] = c["pool_rows"]  # segment past the pool
     with pytest.raises(oracle.OracleError):
         oracle.verify_attn(c["q"], c["k_pool"], c["v_pool"], off, c["k"], c["ctx_len"], bad)
+
+
+def _scatter_pool(c, seed, share=False):
+    """The same case with every pool row moved to a random place and a token-granular cache
+    map [n_bs, ctx + W] pointing at it (DScale Sec. III-D: historyKV gathered through
+    cacheMap).  With share=True request 1's first context rows alias request 0's (a shared
+    prefix)."""
+    rng = np.random.default_rng(seed)
+    hkv, rows, d = c["k_pool"].shape
+    perm = rng.permutation(rows)  # row r moves to perm[r]
+    kp = np.empty_like(c["k_pool"])
+    vp = np.empty_like(c["v_pool"])
+    kp[:, perm] = c["k_pool"]
+    vp[:, perm] = c["v_pool"]
+    n_bs = len(c["k"])
+    stride = int((c["ctx_len"] + c["W"]).max())
+    idx = np.full((n_bs, stride), -1, np.int32)
+    for i in range(n_bs):
+        n = int(c["ctx_len"][i] + c["k"][i])
+        idx[i, :n] = perm[int(c["kv_base"][i]) + np.arange(n)]
+    if share:
+        n = int(min(c["ctx_len"][0], c["ctx_len"][1]))
+        idx[1, :n] = idx[0, :n]
+    return kp, vp, idx
+
+
+@pytest.mark.parametrize("use_new", [True, False])
+def test_cache_map_equals_contiguous_segments(use_new):
+    """Reading rows through a token-granular cache map of a permuted pool gives exactly the
+    contiguous-segment result (the gather is an addressing change only)."""
+    c = _small_case(seed=21, dtype="bf16")
+    off = _offsets(c)
+    kn = c["k_new"] if use_new else None
+    vn = c["v_new"] if use_new else None
+    base = oracle.verify_attn(c["q"], c["k_pool"], c["v_pool"], off, c["k"], c["ctx_len"], c["kv_base"], kn, vn)
+    kp, vp, idx = _scatter_pool(c, 5)
+    mapped = oracle.verify_attn(c["q"], kp, vp, off, c["k"], c["ctx_len"], c["kv_base"], kn, vn, kv_index=idx)
+    end = int(off[-1])
+    assert np.array_equal(base[0][:end], mapped[0][:end]) and np.array_equal(base[1][:end], mapped[1][:end])
+
+
+def test_cache_map_shared_prefix_matches_sdpa():
+    """A cache map whose requests share context rows: every row equals fp64 SDPA over the
+    gathered keys with the request-local causal mask."""
+    c = _small_case(seed=22, dtype="f32", hq=4, hkv=2, d=16, k=(5, 9), ctx=(30, 20), extra_tail=0)
+    off = _offsets(c)
+    kp, vp, idx = _scatter_pool(c, 6, share=True)
+    o, _ = oracle.verify_attn(c["q"], kp, vp, off, c["k"], c["ctx_len"], c["kv_base"], c["k_new"],
+                              c["v_new"], kv_index=idx)
+    q64 = _f64(c["q"])
+    for i in range(2):
+        kk, cx = int(c["k"][i]), int(c["ctx_len"][i])
+        rows = idx[i, :cx]
+        for h in range(4):
+            g = h // 2
+            K = np.concatenate([_f64(kp[g, rows]), _f64(c["k_new"][off[i]:off[i] + kk, g])])
+            V = np.concatenate([_f64(vp[g, rows]), _f64(c["v_new"][off[i]:off[i] + kk, g])])
+            mask = np.zeros((kk, cx + kk), bool)
+            for j in range(kk):
+                mask[j, : cx + j + 1] = True
+            ref = _sdpa(q64[off[i]:off[i] + kk, h], K, V, mask, 1 / np.sqrt(16))
+            assert np.allclose(o[off[i]:off[i] + kk, h], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_cache_map_errors():
+    c = _small_case(seed=23, dtype="bf16")
+    off = _offsets(c)
+    kp, vp, idx = _scatter_pool(c, 7)
+    bad = idx.copy()
+    bad[0, 0] = kp.shape[1]  # a row past the pool
+    with pytest.raises(oracle.OracleError):
+        oracle.verify_attn(c["q"], kp, vp, off, c["k"], c["ctx_len"], c["kv_base"], c["k_new"], c["v_new"],
+                           kv_index=bad)
+    short = idx[:, :3]  # fewer entries than a request's visible positions
+    with pytest.raises(oracle.OracleError):
+        oracle.verify_attn(c["q"], kp, vp, off, c["k"], c["ctx_len"], c["kv_base"], c["k_new"], c["v_new"],
+                           kv_index=short)
