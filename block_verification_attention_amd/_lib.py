@@ -41,6 +41,7 @@ class AttnArgs(ctypes.Structure):
         ("pf_q", P), ("pf_k_new", P), ("pf_v_new", P), ("pf_out", P), ("pf_lse", P),
         ("workspace", P), ("workspace_bytes", ctypes.c_size_t), ("status", P),
         ("main_begin", P), ("main_end", P),
+        ("kv_index", P), ("kv_index_stride", i64),
     ]
 
 

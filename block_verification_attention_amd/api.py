@@ -123,9 +123,9 @@ def _dtype_code(t):
 def attn_args(q, k_pool, v_pool, offsets, k, ctx_len, kv_base, *, W: int, max_ctx: int, out,
               status, lse=None, k_new=None, v_new=None, slot_cache_loc=None, scale: float = 0.0,
               kv_chunk: int = 0, prefill: Prefill | None = None, workspace=None,
-              events=None) -> AttnArgs:
+              events=None, kv_index=None) -> AttnArgs:
     """Builds the dsv_attn_args struct.  q [m_bs, hq, d]; pools [hkv, rows, d] (row stride may
-    exceed d); out like q."""
+    exceed d); out like q; kv_index (optional) [n_bs, stride] int32 token-granular cache map."""
     a = AttnArgs()
     ref = q if q is not None else prefill.q
     a.dtype = _dtype_code(ref)
@@ -172,6 +172,11 @@ def attn_args(q, k_pool, v_pool, offsets, k, ctx_len, kv_base, *, W: int, max_ct
     a.status = status.data_ptr()
     if events is not None:
         a.main_begin, a.main_end = events
+    if kv_index is not None:
+        if kv_index.dtype != torch.int32 or kv_index.dim() != 2 or not kv_index.is_contiguous():
+            raise ValueError("kv_index must be a contiguous [n_bs, stride] int32 tensor")
+        a.kv_index = kv_index.data_ptr()
+        a.kv_index_stride = kv_index.shape[1]
     return a
 
 
@@ -186,7 +191,7 @@ def verify_attn_call(args: AttnArgs, stream=None):
 def verify_attn(q, k_pool, v_pool, offsets, k, ctx_len, kv_base, *, W: int, max_ctx: int,
                 status, out=None, lse=None, k_new=None, v_new=None, slot_cache_loc=None,
                 scale: float = 0.0, kv_chunk: int = 0, prefill: Prefill | None = None,
-                workspace=None, stream=None):
+                workspace=None, stream=None, kv_index=None):
     """Attention over packed verification slots (and an optional prefill set).  Allocates
     `out` and the workspace when they are not given.  Returns (out, lse)."""
     if out is None and q is not None:
@@ -194,7 +199,7 @@ def verify_attn(q, k_pool, v_pool, offsets, k, ctx_len, kv_base, *, W: int, max_
     args = attn_args(q, k_pool, v_pool, offsets, k, ctx_len, kv_base, W=W, max_ctx=max_ctx,
                      out=out, status=status, lse=lse, k_new=k_new, v_new=v_new,
                      slot_cache_loc=slot_cache_loc, scale=scale, kv_chunk=kv_chunk,
-                     prefill=prefill)
+                     prefill=prefill, kv_index=kv_index)
     need = verify_attn_workspace_bytes(args)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=k_pool.device)

@@ -69,7 +69,9 @@ struct AttnParams {
   void *pf_out;
   float *pf_lse;
   int32_t *status;
-
+  // token-granular cache map of the verification set (null: contiguous segments)
+  const int32_t *kv_index;
+  int64_t kv_index_stride;
 };
 
 // Checks request i of the verification set; on success returns 0 and its fields.
@@ -78,11 +80,26 @@ __device__ __forceinline__ int verify_request(const AttnParams &p, int i, int &k
   ki = p.k[i];
   off = p.offsets[i];
   c = p.ctx_len[i];
-  kb = p.kv_base[i];
-  if (ki < 0 || ki > p.W || off < 0 || (int64_t)off + ki > p.m_bs || c < 0 || kb < 0)
+  kb = p.kv_index ? 0 : p.kv_base[i];
+  if (ki < 0 || ki > p.W || off < 0 || (int64_t)off + ki > p.m_bs || c < 0)
     return DSV_STATUS_BAD_REQUEST;
+  if (p.kv_index) return (int64_t)c + ki > p.kv_index_stride ? DSV_STATUS_BAD_REQUEST : 0;
+  if (kb < 0) return DSV_STATUS_BAD_REQUEST;
   if (kb + c + ki > p.pool_rows) return DSV_STATUS_POOL;
   return 0;
+}
+
+// Pool row of position pos of a verification request: its contiguous segment (kb + pos), or
+// with a cache map (kvi = the request's row of kv_index) the mapped row; a mapped row outside
+// the pool flags the status word and reads the nearest pool row instead.
+__device__ __forceinline__ int64_t mapped_row(const AttnParams &p, const int32_t *kvi, int64_t kb, int pos) {
+  if (!kvi) return kb + pos;
+  int64_t r = gload<int32_t>(kvi + pos);
+  if (r < 0 || r >= p.pool_rows) {
+    status_or(p.status, DSV_STATUS_POOL);
+    r = r < 0 ? 0 : p.pool_rows - 1;
+  }
+  return r;
 }
 
 // Splits of a verification request with n_vis visible positions: floor(n_vis / chunk) of them
@@ -213,6 +230,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
   int64_t kb, q_row0;
   const uint16_t *qsrc;
   const uint16_t *knew = nullptr, *vnew = nullptr;
+  const int32_t *kvi = nullptr;  // the request's cache-map row (verification with a cache map)
   if constexpr (!PF) {
     const int bid = blockIdx.x;
     g = bid % p.hkv;
@@ -240,6 +258,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     const int n_vis = c + ki;
     n_splits_i = verify_splits(p, n_vis);
     if (ki == 0 || split >= n_splits_i) return;
+    if (p.kv_index) kvi = p.kv_index + (int64_t)i * p.kv_index_stride;
     r_lo = split * p.chunk;
     r_hi = split == n_splits_i - 1 ? n_vis : r_lo + p.chunk;
     row0 = 0;
@@ -331,9 +350,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
   // constant; boundary tiles: per-lane rows that may come from k_new or be clamped), then one
   // load per piece; the staged data is kept as scalars so that it never forms one wide vector
   // register.
+  const char *kpool_g = static_cast<const char *>(p.k_pool) + g * p.stride_head * 2;
+  const char *vpool_g = static_cast<const char *>(p.v_pool) + g * p.stride_head * 2;
   auto load_tile = [&](int tile_base, Piece (&x)[QPW]) __attribute__((always_inline)) {
     const char *src[QPW];
-    if (tile_base + HV * TILE <= t_hi) {
+    if (kvi) {  // cache map: every row through its mapped pool row
+#pragma unroll
+      for (int u = 0; u < QPW; ++u) {
+        int pos = tile_base + piece_sub(u) * TILE + piece_row(u);
+        pos = pos < t_hi ? pos : t_hi - 1;
+        src[u] = (piece_is_v(u) ? vpool_g : kpool_g) + mapped_row(p, kvi, 0, pos) * row_bytes +
+                 16 * (lane % (D / 8));
+      }
+    } else if (tile_base + HV * TILE <= t_hi) {
       const char *kt = reinterpret_cast<const char *>(kseg) + (size_t)tile_base * row_bytes;
       const char *vt = reinterpret_cast<const char *>(vseg) + (size_t)tile_base * row_bytes;
 #pragma unroll
@@ -499,8 +528,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
       const int isv = e / (16 * (D / 8)), row = (e / (D / 8)) % 16, slot = e % (D / 8);
       xc[b] = Piece{0u, 0u, 0u, 0u};
       if (e < CPH && row < nrows) {
-        const uint16_t *r = knew ? (isv ? vnew : knew) + ((int64_t)(off + row) * p.hkv + g) * D
-                                 : (isv ? vseg : kseg) + (int64_t)(c + row) * row_elems;
+        const uint16_t *r =
+            knew ? (isv ? vnew : knew) + ((int64_t)(off + row) * p.hkv + g) * D
+                 : reinterpret_cast<const uint16_t *>((isv ? vpool_g : kpool_g) +
+                                                      mapped_row(p, kvi, kb, c + row) * row_bytes);
         const u32x4 v = gload_stream<u32x4>(r + 8 * slot);
         xc[b] = Piece{v[0], v[1], v[2], v[3]};
       }
@@ -719,6 +750,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnParams p, int prefill
   const float *vpool = static_cast<const float *>(p.v_pool);
   int c, j, off = 0;
   int64_t kb, qrow;
+  const int32_t *kvi = nullptr;  // cache-map row of a verification request
   const float *knew = nullptr, *vnew = nullptr;
   const float *qsrc;
   float *outp;
@@ -749,6 +781,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnParams p, int prefill
       return;
     }
     if (j >= ki) return;
+    if (p.kv_index) kvi = p.kv_index + (int64_t)i * p.kv_index_stride;
     qrow = off + j;
     qsrc = static_cast<const float *>(p.q);
     outp = static_cast<float *>(p.out);
@@ -789,11 +822,11 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnParams p, int prefill
   const int n = c + j + 1;
   auto krow = [&](int pos) -> const float * {
     if (knew && pos >= c) return knew + ((int64_t)(off + pos - c) * p.hkv + g) * D;
-    return kpool + g * p.stride_head + (kb + pos) * p.stride_row;
+    return kpool + g * p.stride_head + mapped_row(p, kvi, kb, pos) * p.stride_row;
   };
   auto vrow = [&](int pos) -> const float * {
     if (vnew && pos >= c) return vnew + ((int64_t)(off + pos - c) * p.hkv + g) * D;
-    return vpool + g * p.stride_head + (kb + pos) * p.stride_row;
+    return vpool + g * p.stride_head + mapped_row(p, kvi, kb, pos) * p.stride_row;
   };
   float m = -INFINITY, l = 0.f, acc = 0.f;
   for (int base = 0; base < n; base += 256) {
@@ -981,7 +1014,9 @@ extern "C" dsv_status dsv_verify_attn(const dsv_attn_args *a, hipStream_t stream
     if ((a->k_new == nullptr) != (a->v_new == nullptr)) return DSV_ERR_INVALID_ARG;
     if (a->k_new && !a->slot_cache_loc) return DSV_ERR_INVALID_ARG;
     if (a->kv_chunk < 0 || a->kv_chunk % kTileKV) return DSV_ERR_INVALID_ARG;
+    if (a->kv_index && a->kv_index_stride < 1) return DSV_ERR_INVALID_ARG;
   }
+  if (a->kv_index && prefill) return DSV_ERR_UNSUPPORTED;
   if (prefill) {
     if (!a->pf_q_start || !a->pf_q_len || !a->pf_ctx_len || !a->pf_kv_base || !a->pf_q ||
         !a->pf_out || a->pf_max_len < 1 || a->pf_q_rows < 0)
@@ -1042,6 +1077,8 @@ extern "C" dsv_status dsv_verify_attn(const dsv_attn_args *a, hipStream_t stream
   p.pf_out = a->pf_out;
   p.pf_lse = a->pf_lse;
   p.status = a->status;
+  p.kv_index = verify ? a->kv_index : nullptr;
+  p.kv_index_stride = a->kv_index_stride;
   if (verify && a->dtype == DSV_F32) p.n_splits = 1, p.chunk = a->max_ctx + a->W;
 
   const int D = a->d;

@@ -230,6 +230,18 @@ typedef struct dsv_attn_args {
      these events on `stream` immediately before and after the verification
      attention kernel (the split-KV merge, if any, comes after main_end). */
   hipEvent_t main_begin, main_end;
+
+  /* Optional token-granular cache map of the verification set (the pages'
+     cacheMap / historyKV gather, DScale Sec. III-D): when non-null, position
+     p of request i (0 <= p < ctx_len[i] + k[i]) is pool row
+     kv_index[i * kv_index_stride + p] instead of kv_base[i] + p.  Rows are
+     read for the context and, when k_new is null, for the candidates; a
+     row outside [0, pool_rows) sets DSV_STATUS_POOL and reads row 0 or the
+     last row instead; ctx_len[i] + k[i] > kv_index_stride makes request i
+     invalid (DSV_STATUS_BAD_REQUEST).  kv_base is then unused by this call.
+     Not supported together with a prefill set or with DSV_F32 prefill. */
+  const int32_t *kv_index;  /* [n_bs][kv_index_stride] or null */
+  int64_t kv_index_stride;
 } dsv_attn_args;
 
 /* sizeof(dsv_attn_args) as compiled into the library (binding check). */
