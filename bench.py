@@ -34,7 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-PROFILED_KERNEL = "attn_bf16_kernel<128, 8, false, 64, 2>"
+PROFILED_KERNEL = "attn_bf16_kernel<128, 8, false, 64, 2, false>"
 # HBM bytes per launch of that kernel on this workload, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs (profiles/attn_verify_cfg3_hbm_traffic.md, calibrated there against the
 # streaming-read probe and a pool copy), valid for the kernel source with this SHA-256 only.
@@ -343,6 +343,31 @@ def main():
     pool_bytes = 2 * kp0.numel() * 2
     res["roofline"]["stream_read_ceiling_GBs"] = pool_bytes / (probe_avg * 1e-3) / 1e9
     res["roofline"]["frac_of_ceiling"] = achieved / res["roofline"]["stream_read_ceiling_GBs"]
+    # token-granular cache map (kv_index): the same launch with every K/V row read through a
+    # per-position row table -- the identity map, and rows scattered over the whole pool (a
+    # random permutation, so every pool row is still read once)
+    def time_mapped(idx_t):
+        evs = ev.create(2 * n_total)
+        margs = [make_args(s, (evs[2 * s].value, evs[2 * s + 1].value)) for s in range(n_total)]
+        for a in margs:
+            a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+            a.kv_index, a.kv_index_stride = idx_t.data_ptr(), idx_t.shape[1]
+        for s in range(n_total):
+            dsv.verify_attn_call(margs[s])
+        torch.cuda.synchronize()
+        t = float(np.mean([ev.elapsed_ms(evs[2 * s], evs[2 * s + 1]) for s in range(args.warmup, n_total)]))
+        ev.destroy(evs)
+        return t * 1e3
+    stride_map = int((c["ctx_len"] + c["k"]).max())
+    pos = np.arange(stride_map, dtype=np.int64)[None, :]
+    ident = (c["kv_base"][:, None] + pos).astype(np.int64)
+    rows = c["k_pool"].shape[1]
+    perm = np.random.default_rng(77).permutation(rows)
+    maps = {"identity": np.minimum(ident, rows - 1), "scattered": perm[np.minimum(ident, rows - 1)]}
+    res["cache_map"] = {"contiguous_us": attn_avg_ms * 1e3}
+    for name, m in maps.items():
+        res["cache_map"][f"{name}_us"] = time_mapped(torch.from_numpy(m.astype(np.int32)).to(dev))
+    res["cache_map"]["scattered_GBs"] = kvb / (res["cache_map"]["scattered_us"] * 1e-6) / 1e9
     res["allocator"] = time_allocator(dev)
     if args.cpu_sample > 0:
         res["cpu_baseline"] = cpu_baseline(c, args.cpu_sample)

@@ -198,7 +198,7 @@ constexpr int waves_per_eu_hint() {
   return (NW <= 2 || (D == 256 && NW <= 4)) ? 1 : (NW <= 8 ? 2 : 1);
 }
 
-template <int D, int NW, bool PF, int TILE, int HV>
+template <int D, int NW, bool PF, int TILE, int HV, bool MAP>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_per_eu_hint<D, NW>()))) void attn_bf16_kernel(AttnParams p) {
   constexpr int RPC = 1024 / (2 * D);        // rows per 1 KB wave load
   constexpr int NCK = TILE / RPC;            // wave loads per tensor per tile
@@ -209,6 +209,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
   constexpr int STAGE_BYTES = HV * SUB_BYTES;
   constexpr int NWH = NW / HV;               // waves per KV half
   static_assert(!PF || HV == 1, "prefill stacks its waves along the query rows");
+  static_assert(!PF || !MAP, "the cache map applies to the verification set");
   static_assert(NW % HV == 0, "wave halves");
   constexpr int DB = D / 16;
   constexpr int KS = D / 32;
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     const int n_vis = c + ki;
     n_splits_i = verify_splits(p, n_vis);
     if (ki == 0 || split >= n_splits_i) return;
-    if (p.kv_index) kvi = p.kv_index + (int64_t)i * p.kv_index_stride;
+    if (MAP) kvi = p.kv_index + (int64_t)i * p.kv_index_stride;
     r_lo = split * p.chunk;
     r_hi = split == n_splits_i - 1 ? n_vis : r_lo + p.chunk;
     row0 = 0;
@@ -352,15 +353,32 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
   // register.
   const char *kpool_g = static_cast<const char *>(p.k_pool) + g * p.stride_head * 2;
   const char *vpool_g = static_cast<const char *>(p.v_pool) + g * p.stride_head * 2;
+  // Cache map (MAP): the map entries of the next stage's rows are fetched when a stage's data
+  // loads go out (stages are loaded in order), so a stage's data loads never wait for their
+  // own map entries.
+  int32_t map_next[MAP ? QPW : 1];
+  int map_next_base = -1;
+  auto fetch_map = [&](int tile_base) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < QPW; ++u) {
+      int pos = tile_base + piece_sub(u) * TILE + piece_row(u);
+      pos = pos < t_hi ? pos : t_hi - 1;
+      map_next[u] = gload<int32_t>(kvi + pos);
+    }
+    map_next_base = tile_base;
+  };
   auto load_tile = [&](int tile_base, Piece (&x)[QPW]) __attribute__((always_inline)) {
     const char *src[QPW];
-    if (kvi) {  // cache map: every row through its mapped pool row
+    if constexpr (MAP) {  // cache map: every row through its mapped pool row
+      if (map_next_base != tile_base) fetch_map(tile_base);
 #pragma unroll
       for (int u = 0; u < QPW; ++u) {
-        int pos = tile_base + piece_sub(u) * TILE + piece_row(u);
-        pos = pos < t_hi ? pos : t_hi - 1;
-        src[u] = (piece_is_v(u) ? vpool_g : kpool_g) + mapped_row(p, kvi, 0, pos) * row_bytes +
-                 16 * (lane % (D / 8));
+        int64_t r = map_next[u];
+        if (r < 0 || r >= p.pool_rows) {
+          status_or(p.status, DSV_STATUS_POOL);
+          r = r < 0 ? 0 : p.pool_rows - 1;
+        }
+        src[u] = (piece_is_v(u) ? vpool_g : kpool_g) + r * row_bytes + 16 * (lane % (D / 8));
       }
     } else if (tile_base + HV * TILE <= t_hi) {
       const char *kt = reinterpret_cast<const char *>(kseg) + (size_t)tile_base * row_bytes;
@@ -383,6 +401,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
         const u32x4 v = gload_stream<u32x4>(src[u]);
         x[u] = Piece{v[0], v[1], v[2], v[3]};
       }
+    }
+    if constexpr (MAP) {
+      if (tile_base + HV * TILE < t_hi) fetch_map(tile_base + HV * TILE);
     }
   };
   auto store_tile = [&](const Piece (&x)[QPW], int stage) __attribute__((always_inline)) {
@@ -940,11 +961,11 @@ template <> struct TileCfg<64> { static constexpr int TILE = 64; };
 template <> struct TileCfg<128> { static constexpr int TILE = 64; };
 template <> struct TileCfg<256> { static constexpr int TILE = 32; };
 
-template <int D, int NW, bool PF, int HV = 1>
-static bool launch_attn(const AttnParams &p, int grid, hipStream_t s) {
+template <int D, int NW, bool PF, int HV = 1, bool MAP = false>
+static bool launch_attn_k(const AttnParams &p, int grid, hipStream_t s) {
   constexpr int TILE = TileCfg<D>::TILE;
   constexpr size_t shm = (size_t)2 * HV * 2 * TILE * D * sizeof(uint16_t);
-  auto kern = attn_bf16_kernel<D, NW, PF, TILE, HV>;
+  auto kern = attn_bf16_kernel<D, NW, PF, TILE, HV, MAP>;
   // once per kernel (idempotent), so that a captured call contains launches only
   static bool lds_limit_set = false;
   if (!lds_limit_set) {
@@ -955,6 +976,16 @@ static bool launch_attn(const AttnParams &p, int grid, hipStream_t s) {
   }
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), shm, s, p);
   return true;
+}
+
+// The cache-map variant is a separate instantiation, so that the contiguous kernel carries
+// none of its registers.
+template <int D, int NW, bool PF, int HV = 1>
+static bool launch_attn(const AttnParams &p, int grid, hipStream_t s) {
+  if constexpr (!PF) {
+    if (p.kv_index) return launch_attn_k<D, NW, PF, HV, true>(p, grid, s);
+  }
+  return launch_attn_k<D, NW, PF, HV, false>(p, grid, s);
 }
 
 template <int D>
