@@ -17,6 +17,8 @@ full definitions):
 * ``prefill_attn``: the wide-tile prefill path of Sec. III-B.
 * ``accept``: DScale Sec. III-D "Prefix verifier" (greedy), DFlash-Mini-Lab
   exact-prefix acceptance with a non-drafted anchor.
+* ``accept_sample``: the same passage's sampling rule (accept with P(x), on the
+  first rejection draw from P without x, renormalised).
 * ``top2_margin``: the Top1-Top2 draft logit gap of DScale Fig. 4 and the
   DFlash7-ACT margin of DFlash-Mini-Lab.
 """
@@ -81,6 +83,7 @@ def _load():
         lib.oracle_argmax_rows.argtypes = [i64, i64, P, P]
         lib.oracle_accept.argtypes = [i32, i32, i32] + [P] * 8
         lib.oracle_top2_margin.argtypes = [i64, i64, P, P, P]
+        lib.oracle_accept_sample.argtypes = [i32, i32, i32, i64, P, dbl] + [P] * 12
         lib.oracle_threads.argtypes = []
         lib.oracle_allocate.argtypes = [i32, i32, i32, i32, P, P, P]
         _lib = lib
@@ -374,6 +377,39 @@ def accept(logits, slot_tok, offsets, k, W: int) -> dict:
     _check(lib.oracle_accept(n_bs, m_bs, W, _p(offsets), _p(k), _p(slot_tok), _p(slot_argmax),
                              _p(out["accepted"]), _p(out["bonus"]), _p(out["progress"]),
                              _p(out["out_tokens"])))
+    return out
+
+
+def accept_sample(logits, slot_tok, offsets, k, W: int, temperature: float, u_accept, u_draw) -> dict:
+    """Sampling-mode prefix verification (DScale Sec. III-D "Prefix verifier") at temperature T
+    with the caller's uniforms: u_accept [m_bs] (row s tests the candidate at slot s + 1),
+    u_draw [n_bs] (one successor draw per request).  Returns accepted, bonus, progress,
+    out_tokens, p_cand (P of the tested candidate per row, -1 on a request's last row) and the
+    decision margins acc_margin [m_bs] / draw_margin [n_bs] (NaN where no decision was
+    taken)."""
+    lib = _load()
+    logits = _c(logits, np.float32)
+    m_bs, vocab = logits.shape
+    offsets = _c(offsets, np.int32)
+    k = _c(k, np.int32)
+    n_bs = k.shape[0]
+    slot_tok = _c(slot_tok, np.int32)
+    u_accept = _c(u_accept, np.float32)
+    u_draw = _c(u_draw, np.float32)
+    assert slot_tok.shape[0] >= m_bs and u_accept.shape[0] >= m_bs and u_draw.shape[0] >= n_bs
+    out = dict(
+        accepted=np.zeros(n_bs, np.int32),
+        bonus=np.zeros(n_bs, np.int32),
+        progress=np.zeros(n_bs, np.int32),
+        out_tokens=np.zeros((n_bs, W), np.int32),
+        p_cand=np.full(m_bs, np.nan),
+        acc_margin=np.zeros(m_bs),
+        draw_margin=np.zeros(n_bs),
+    )
+    _check(lib.oracle_accept_sample(
+        n_bs, m_bs, W, vocab, _p(logits), float(temperature), _p(offsets), _p(k), _p(slot_tok),
+        _p(u_accept), _p(u_draw), _p(out["accepted"]), _p(out["bonus"]), _p(out["progress"]),
+        _p(out["out_tokens"]), _p(out["p_cand"]), _p(out["acc_margin"]), _p(out["draw_margin"])))
     return out
 
 

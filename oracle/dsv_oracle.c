@@ -521,6 +521,136 @@ int oracle_accept(int n_bs, int m_bs, int W, const int32_t *offsets, const int32
 }
 
 /* ------------------------------------------------------------------------ */
+/* Sampling-mode prefix verifier (DScale Sec. III-D "Prefix verifier": a     */
+/* deterministic top-1 draft x is accepted with probability P(x); at the     */
+/* first rejection the successor is drawn from P with x removed and the      */
+/* remaining mass renormalised; when every candidate passes it is drawn from */
+/* the unmodified P; row offset_i + a_i supplies the successor).             */
+/*                                                                            */
+/* P_s = softmax(logits[s] / T), evaluated in double as                       */
+/* exp((l_v - max l) / T) / sum_u exp((l_u - max l) / T).  Candidate j >= 1   */
+/* of request i (x = slot_tok[off + j]) is tested by row s = off + j - 1 and  */
+/* passes when u_accept[s] < P_s(x).  a_i = number of passes before the      */
+/* first failure.  The successor is drawn from row off + a_i with weights    */
+/* w_v = P(v), w_x = 0 on a rejection, by the inverse CDF at u_draw[i]: the  */
+/* smallest y with u * S < w_0 + ... + w_y (S = sum of w, index order); if   */
+/* rounding leaves no such y, the last y with w_y > 0.  Outputs as in the    */
+/* greedy verifier.  p_cand[s] = P_s(x) for rows that test a candidate, -1   */
+/* for other rows of the request.  Diagnostics for the tests: acc_margin[s]  */
+/* = |u_accept[s] - P_s(x)| for every test taken (NaN otherwise) and         */
+/* draw_margin[i] = the distance of u * S to the nearer boundary of the      */
+/* drawn token's interval, divided by S.  A candidate token outside         */
+/* [0, vocab) has probability 0.  A NaN or +inf in a row of an active        */
+/* request, or a row with no finite entry, is an error.                       */
+/* ------------------------------------------------------------------------ */
+static int softmax_row(const float *x, int64_t vocab, double T, double *p) {
+  double m = -INFINITY;
+  for (int64_t v = 0; v < vocab; ++v) {
+    if (isnan(x[v]) || x[v] == INFINITY) return OR_ERR_NAN;
+    if ((double)x[v] > m) m = (double)x[v];
+  }
+  if (m == -INFINITY) return OR_ERR_NAN;
+  double z = 0.0;
+  for (int64_t v = 0; v < vocab; ++v) {
+    p[v] = exp(((double)x[v] - m) / T);
+    z += p[v];
+  }
+  for (int64_t v = 0; v < vocab; ++v) p[v] /= z;
+  return OR_OK;
+}
+
+int oracle_accept_sample(int n_bs, int m_bs, int W, int64_t vocab, const float *logits,
+                         double T, const int32_t *offsets, const int32_t *k,
+                         const int32_t *slot_tok, const float *u_accept, const float *u_draw,
+                         int32_t *accepted, int32_t *bonus, int32_t *progress,
+                         int32_t *out_tokens, double *p_cand, double *acc_margin,
+                         double *draw_margin) {
+  if (vocab < 1 || !(T > 0.0) || isinf(T)) return OR_ERR_ARG;
+  for (int i = 0; i < n_bs; ++i)
+    if (k[i] < 0 || k[i] > W || offsets[i] < 0 || offsets[i] + k[i] > m_bs) return OR_ERR_K;
+  for (int64_t s = 0; s < m_bs; ++s) acc_margin[s] = NAN;
+  int err = OR_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int i = 0; i < n_bs; ++i) {
+    for (int t = 0; t < W; ++t) out_tokens[(int64_t)i * W + t] = -1;
+    draw_margin[i] = NAN;
+    accepted[i] = 0;
+    bonus[i] = -1;
+    progress[i] = 0;
+    if (k[i] == 0) continue;
+    const int off = offsets[i];
+    double *p = malloc((size_t)vocab * sizeof(double));
+    double *prow = malloc((size_t)k[i] * sizeof(double));
+    int bad = 0;
+    /* P_s(x) for every row that tests a candidate */
+    for (int j = 0; j < k[i] && !bad; ++j) {
+      const int s = off + j;
+      bad = softmax_row(logits + (int64_t)s * vocab, vocab, T, p);
+      if (bad) break;
+      if (j + 1 < k[i]) {
+        const int32_t x = slot_tok[s + 1];
+        prow[j] = x >= 0 && x < vocab ? p[x] : 0.0;
+      } else {
+        prow[j] = -1.0;
+      }
+      p_cand[s] = prow[j];
+    }
+    if (bad) {
+#pragma omp atomic write
+      err = bad;
+      free(p);
+      free(prow);
+      continue;
+    }
+    int a = 0;
+    int rejected = 0;
+    while (a + 1 < k[i]) {
+      const int s = off + a;
+      acc_margin[s] = fabs((double)u_accept[s] - prow[a]);
+      if ((double)u_accept[s] < prow[a]) {
+        ++a;
+      } else {
+        rejected = 1;
+        break;
+      }
+    }
+    /* successor from row off + a, the rejected draft removed */
+    const int s = off + a;
+    softmax_row(logits + (int64_t)s * vocab, vocab, T, p);
+    if (rejected && slot_tok[s + 1] >= 0 && slot_tok[s + 1] < vocab) p[slot_tok[s + 1]] = 0.0;
+    double S = 0.0;
+    for (int64_t v = 0; v < vocab; ++v) S += p[v];
+    const double target = (double)u_draw[i] * S;
+    int64_t y = -1, last = -1;
+    double below = 0.0, cum = 0.0;
+    for (int64_t v = 0; v < vocab; ++v) {
+      if (p[v] > 0.0) last = v;
+      below = cum;
+      cum += p[v];
+      if (target < cum) {
+        y = v;
+        break;
+      }
+    }
+    if (y < 0) {
+      y = last;
+      draw_margin[i] = 0.0;
+    } else {
+      const double d0 = target - below, d1 = cum - target;
+      draw_margin[i] = (d0 < d1 ? d0 : d1) / S;
+    }
+    accepted[i] = a;
+    bonus[i] = (int32_t)y;
+    progress[i] = 1 + a;
+    for (int t = 0; t < a; ++t) out_tokens[(int64_t)i * W + t] = slot_tok[off + 1 + t];
+    out_tokens[(int64_t)i * W + a] = (int32_t)y;
+    free(p);
+    free(prow);
+  }
+  return err;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Draft top-1 / top-2 margin (DScale Sec. II-B, Fig. 4: "mean Top1-Top2     */
 /* logit gap"; DFlash-Mini-Lab DFlash7-ACT margin).  For each row, top1 is   */
 /* the largest value and top2 the second element of the row sorted in       */
