@@ -12,6 +12,8 @@ from ._lib import DsvError, MAX_W, STATUS_BAD_REQUEST, STATUS_BUDGET, STATUS_NAN
 from .api import (
     Prefill,
     accept,
+    accept_sample,
+    accept_sample_workspace_bytes,
     allocate_pack,
     accept_workspace_bytes,
     attn_args,
@@ -24,7 +26,8 @@ from .api import (
 
 __all__ = [
     "DsvError", "MAX_W", "STATUS_BAD_REQUEST", "STATUS_BUDGET", "STATUS_NAN", "STATUS_POOL",
-    "STATUS_PREFILL", "Prefill", "accept", "accept_workspace_bytes", "allocate_pack", "attn_args", "new_status",
+    "STATUS_PREFILL", "Prefill", "accept", "accept_sample", "accept_sample_workspace_bytes",
+    "accept_workspace_bytes", "allocate_pack", "attn_args", "new_status",
     "pack_slots", "verify_attn", "verify_attn_call", "verify_attn_workspace_bytes",
 ]
 

@@ -1,7 +1,8 @@
 """Thin PyTorch-facing binding of libdsv: argument marshalling only.
 
 Every step runs in the HIP kernels of libdsv.so; PyTorch provides device memory and the
-stream.  Names follow the C ABI (include/dsv.h): pack_slots, verify_attn, accept.
+stream.  Names follow the C ABI (include/dsv.h): pack_slots, allocate_pack, verify_attn,
+accept, accept_sample.
 """
 from __future__ import annotations
 
@@ -249,4 +250,45 @@ def accept(*, n_bs: int, W: int, status, target_logits=None, slot_tok=None, offs
         _ptr(o.get("margin")), _ptr(o.get("draft_top1")), _ptr(workspace),
         workspace.numel() if workspace is not None else 0, _ptr(status), _stream(stream)),
         "dsv_accept")
+    return o
+
+
+# ---------------------------------------------------------------------------
+# dsv_accept_sample
+# ---------------------------------------------------------------------------
+def accept_sample_workspace_bytes(n_bs, m_bs, vocab) -> int:
+    return int(_lib.load().dsv_accept_sample_workspace_bytes(n_bs, m_bs, vocab))
+
+
+def accept_sample(*, n_bs: int, W: int, status, target_logits, temperature: float, slot_tok,
+                  offsets, k, u_accept, u_draw, out=None, workspace=None, stream=None) -> dict:
+    """Sampling-mode prefix verification over target_logits [m_bs, vocab] at `temperature`,
+    with the caller's uniforms u_accept [m_bs] and u_draw [n_bs].  Returns accepted, bonus,
+    progress, out_tokens and p_cand."""
+    lib = _lib.load()
+    dev = status.device
+    _need(target_logits, torch.float32, "target_logits", dev)
+    m_bs, vocab = target_logits.shape
+    for t, dt, nm in ((slot_tok, torch.int32, "slot_tok"), (offsets, torch.int32, "offsets"),
+                      (k, torch.int32, "k"), (u_accept, torch.float32, "u_accept"),
+                      (u_draw, torch.float32, "u_draw")):
+        _need(t, dt, nm, dev)
+    if slot_tok.numel() < m_bs or u_accept.numel() < m_bs or u_draw.numel() < n_bs:
+        raise ValueError("slot_tok and u_accept need m_bs entries, u_draw n_bs")
+    if offsets.numel() < n_bs + 1 or k.numel() < n_bs:
+        raise ValueError("offsets needs n_bs + 1 entries, k n_bs")
+    o = out if out is not None else {}
+    for nm in ("accepted", "bonus", "progress"):
+        o.setdefault(nm, torch.empty(n_bs, dtype=torch.int32, device=dev))
+    o.setdefault("out_tokens", torch.empty((n_bs, W), dtype=torch.int32, device=dev))
+    o.setdefault("p_cand", torch.full((m_bs,), float("nan"), dtype=torch.float32, device=dev))
+    need = accept_sample_workspace_bytes(n_bs, m_bs, vocab)
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    check(lib.dsv_accept_sample(
+        n_bs, m_bs, W, vocab, _ptr(target_logits), float(temperature), _ptr(slot_tok),
+        _ptr(offsets), _ptr(k), _ptr(u_accept), _ptr(u_draw), _ptr(o["accepted"]),
+        _ptr(o["bonus"]), _ptr(o["progress"]), _ptr(o.get("out_tokens")), _ptr(o.get("p_cand")),
+        _ptr(workspace), workspace.numel() if workspace is not None else 0, _ptr(status),
+        _stream(stream)), "dsv_accept_sample")
     return o

@@ -294,6 +294,49 @@ dsv_status dsv_accept(int32_t n_bs, int32_t m_bs, int32_t W, int32_t vocab,
                       hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* dsv_accept_sample -- sampling-mode prefix verifier and output builder     */
+/*                                                                            */
+/* DScale Sec. III-D (Prefix verifier: with P the target's next-token        */
+/* distribution, a deterministic top-1 draft x is accepted with probability  */
+/* P(x); at the first rejection the successor is drawn from P with x removed */
+/* and the rest renormalised; when every candidate passes, from the          */
+/* unmodified P; row offset_i + a_i supplies the successor).                 */
+/*                                                                            */
+/* target_logits [m_bs][vocab] f32; P_s = softmax(target_logits[s] / T),    */
+/*   0 < temperature < inf.  Candidate j >= 1 of request i (x =              */
+/*   slot_tok[off_i + j]) is tested by row s = off_i + j - 1 and passes when  */
+/*   u_accept[s] < P_s(x) (P_s in fp32; a token outside [0, vocab) has       */
+/*   P = 0).  a_i = passes before the first failure.  The successor is drawn */
+/*   from row off_i + a_i with weights w_v = exp((l_v - max l) / T) in fp64, */
+/*   w_x = 0 after a failure, by the inverse CDF at u_draw[i]: the smallest  */
+/*   v whose cumulative weight in index order exceeds u_draw[i] * sum(w)      */
+/*   (the last v with w_v > 0 if rounding leaves none).  Uniforms are the    */
+/*   caller's, in [0, 1): u_accept [m_bs], u_draw [n_bs].                     */
+/* Outputs as dsv_accept: accepted, bonus (successor), progress = 1 + a_i,   */
+/*   out_tokens [n_bs][W] (may be null) = accepted drafts, successor, -1.    */
+/*   p_cand [m_bs] (may be null): P_s(x) for each row that tests a           */
+/*   candidate, -1 for a request's last row, other rows unchanged.           */
+/*   k_i = 0: accepted 0, bonus -1, progress 0, out_tokens -1.                */
+/* Workspace: dsv_accept_sample_workspace_bytes(n_bs, m_bs, vocab) bytes,    */
+/*   256-byte aligned device memory, no initialisation needed.               */
+/* Errors  host: DSV_ERR_INVALID_ARG (sizes, W outside [1, DSV_MAX_W], a      */
+/*   temperature that is not finite and positive, a missing pointer),        */
+/*   DSV_ERR_WORKSPACE.  Device: invalid k_i/offsets: DSV_STATUS_BAD_REQUEST; */
+/*   a NaN or +inf logit, or no finite logit, in a row of request i:         */
+/*   DSV_STATUS_NAN; both give accepted -1, bonus -1, progress 0 and         */
+/*   out_tokens -1 for that request.                                          */
+/* ------------------------------------------------------------------------ */
+size_t dsv_accept_sample_workspace_bytes(int32_t n_bs, int32_t m_bs, int32_t vocab);
+
+dsv_status dsv_accept_sample(int32_t n_bs, int32_t m_bs, int32_t W, int32_t vocab,
+                             const float *target_logits, float temperature,
+                             const int32_t *slot_tok, const int32_t *offsets, const int32_t *k,
+                             const float *u_accept, const float *u_draw, int32_t *accepted,
+                             int32_t *bonus, int32_t *progress, int32_t *out_tokens,
+                             float *p_cand, void *workspace, size_t workspace_bytes,
+                             int32_t *status, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* dsv_probe_stream_read -- measurement helper (not part of the method)      */
 /*                                                                            */
 /* Reads `bytes` (rounded down to 16) of device memory at `buf` (16-byte     */

@@ -125,6 +125,38 @@ def planted_logits(g, k, vocab: int, m_bs: int, accepted, block_tokens, W: int =
     return np.ascontiguousarray(logits), bt.astype(np.int32), planted.astype(np.int32)
 
 
+def sampling_logits(g, k, vocab: int, m_bs: int, block_tokens, boost=(4.0, 12.0),
+                    p_random: float = 0.2, W: int = W_BLOCK):
+    """Target logits [m_bs, vocab] ~ N(0,1) for sampling-mode verification, and block tokens
+    whose drafts are the target's likely picks: for draft j >= 1 of request i, with probability
+    1 - p_random a random token t gets the logit (row max + U(boost)) in the row that predicts
+    it (row j - 1 of the request) and becomes the draft; otherwise the draft is a random token
+    with no boost.  The boost range sets how much of the row's mass the draft carries (the
+    defaults spread it over (0, 1) at a 151,936-token vocabulary and unit temperature).
+
+    Returns (logits, block_tokens)."""
+    n = len(k)
+    blocks = []
+    bt = np.array(block_tokens, np.int64, copy=True)
+    for i in range(n):
+        rows = g.standard_normal((int(k[i]), vocab), dtype=np.float32)
+        for j in range(1, int(k[i])):
+            t = int(g.integers(vocab))
+            if g.random() >= p_random:
+                rows[j - 1, t] = rows[j - 1].max() + np.float32(g.uniform(*boost))
+            bt[i, j] = t
+        blocks.append(rows)
+    used = int(sum(int(x) for x in k))
+    tail = g.standard_normal((m_bs - used, vocab), dtype=np.float32)
+    logits = np.concatenate(blocks + [tail], axis=0) if n else tail
+    return np.ascontiguousarray(logits), bt.astype(np.int32)
+
+
+def uniforms(g, n: int) -> np.ndarray:
+    """n fp32 uniforms in [0, 1) (24-bit resolution)."""
+    return g.random(n, dtype=np.float32)
+
+
 def make_case(
     seed_config: int,
     *,
