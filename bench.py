@@ -137,6 +137,74 @@ def time_allocator(dev, iters: int = 50):
     return out
 
 
+def time_sampling(dev, copies: int, iters: int = 20):
+    """Sampling-mode verifier (dsv_accept_sample) next to the greedy verifier (dsv_accept) on
+    the full-width batch: 8 requests x 16 slots, target logits [128, 151936] fp32 at T = 1,
+    drafts that are the target's likely picks (seeded synthetic logits, boosted so that about
+    five drafts per request pass), seeded uniforms.  The logits are rotated over `copies`
+    device copies so that the Infinity Cache cannot serve them between calls; device
+    microseconds per call from HIP-graph replays of back-to-back calls, and the logits sweep
+    rate that implies (one read of the 77.8 MB of logits per call)."""
+    import numpy as np
+    import torch
+    import block_verification_attention_amd as dsv
+    import workloads as wl
+    g = np.random.default_rng(6000)
+    n_bs, W, vocab = 8, 16, 151936
+    k = np.full(n_bs, W, np.int32)
+    bt = g.integers(0, vocab, (n_bs, W)).astype(np.int32)
+    logits, bt = wl.sampling_logits(g, k, vocab, n_bs * W, bt, boost=(8.0, 12.0), p_random=0.05)
+    slot_tok = torch.from_numpy(bt.reshape(-1)).to(dev)  # W slots per request: packed layout
+    offsets = torch.from_numpy(np.arange(n_bs + 1, dtype=np.int32) * W).to(dev)
+    kd = torch.from_numpy(k).to(dev)
+    lg0 = torch.from_numpy(logits).to(dev)
+    lgs = [lg0] + [lg0.clone() for _ in range(copies - 1)]
+    u_acc = torch.from_numpy(wl.uniforms(g, n_bs * W)).to(dev)
+    u_draw = torch.from_numpy(wl.uniforms(g, n_bs)).to(dev)
+    st = dsv.new_status(dev)
+    so = dsv.accept_sample(n_bs=n_bs, W=W, status=st, target_logits=lg0, temperature=1.0,
+                           slot_tok=slot_tok, offsets=offsets, k=kd, u_accept=u_acc, u_draw=u_draw)
+    sws = torch.empty(max(dsv.accept_sample_workspace_bytes(n_bs, n_bs * W, vocab), 256),
+                      dtype=torch.uint8, device=dev)
+    go = dsv.accept(n_bs=n_bs, W=W, status=st, target_logits=lg0, slot_tok=slot_tok,
+                    offsets=offsets, k=kd)
+    gws = torch.empty(max(dsv.accept_workspace_bytes(n_bs * W, vocab, 0, 0, 0), 256),
+                      dtype=torch.uint8, device=dev)
+    calls = {
+        "sample_us": lambda j: dsv.accept_sample(
+            n_bs=n_bs, W=W, status=st, target_logits=lgs[j % copies], temperature=1.0,
+            slot_tok=slot_tok, offsets=offsets, k=kd, u_accept=u_acc, u_draw=u_draw, out=so,
+            workspace=sws),
+        "greedy_us": lambda j: dsv.accept(
+            n_bs=n_bs, W=W, status=st, target_logits=lgs[j % copies], slot_tok=slot_tok,
+            offsets=offsets, k=kd, out=go, workspace=gws),
+    }
+    res = {}
+    for name, fn in calls.items():
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for j in range(3):
+                fn(j)
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=s):
+                for j in range(iters):
+                    fn(j)
+        torch.cuda.current_stream().wait_stream(s)
+        gr.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(5):
+            gr.replay()
+        b.record()
+        torch.cuda.synchronize()
+        res[name] = a.elapsed_time(b) * 1e3 / (5 * iters)
+    res["sample_sweep_GBs"] = logits.nbytes / (res["sample_us"] * 1e-6) / 1e9
+    res["mean_progress"] = float(so["progress"].float().mean().item())
+    res["status"] = int(st.item())
+    return res
+
+
 def cpu_baseline(case, n_req_sample: int):
     """The oracle (pack + fp64 attention + greedy accept) on the first n_req_sample requests."""
     import numpy as np
@@ -369,6 +437,7 @@ def main():
         res["cache_map"][f"{name}_us"] = time_mapped(torch.from_numpy(m.astype(np.int32)).to(dev))
     res["cache_map"]["scattered_GBs"] = kvb / (res["cache_map"]["scattered_us"] * 1e-6) / 1e9
     res["allocator"] = time_allocator(dev)
+    res["sampling"] = time_sampling(dev, args.copies)
     if args.cpu_sample > 0:
         res["cpu_baseline"] = cpu_baseline(c, args.cpu_sample)
     print(json.dumps(res))

@@ -223,21 +223,42 @@ __global__ __launch_bounds__(kSmpThreads) void sample_draw_kernel(
     const bool ok = ki >= 0 && ki <= W && off >= 0 && (int64_t)off + ki <= end;
     SampleState r{ok ? (ki == 0 ? 0 : 1) : 3, 0, -1, 0u};
     if (ok && ki > 0) {
+      // lane j tests the candidate of row off + j: its loads go out first
       const int j = lane;
       const int64_t row = (int64_t)off + j;
-      float M = -INFINITY, S = 0.f;
-      if (j < ki)
-        for (int q = 0; q < nc1; ++q) {
-          const SoftStat z = stats[row * nc1 + q];
-          stat_merge(M, S, z.m, z.s, c);
-        }
-      const bool row_bad = j < ki && (S != S || M == -INFINITY);
       const bool tests = j + 1 < ki;
       const int32_t x = tests ? slot_tok[row + 1] : -1;
+      const bool in_vocab = x >= 0 && x < vocab;
+      const float lx = tests && in_vocab ? logits[row * vocab + x] : 0.f;
+      const float ua = tests ? u_accept[row] : 0.f;
+      // four lanes per row merge its chunk statistics: lane 4r + q takes chunks q, q + 4, ...,
+      // with the loads of up to four chunks in flight before any merge
+      const int jr = lane >> 2, q0 = lane & 3;
+      float M = -INFINITY, S = 0.f;
+      if (jr < ki) {
+        const int64_t rrow = (int64_t)off + jr;
+        for (int base = q0; base < nc1; base += 16) {
+          SoftStat z[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int q = base + 4 * u;
+            z[u] = q < nc1 ? stats[rrow * nc1 + q] : SoftStat{-INFINITY, 0.f};
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) stat_merge(M, S, z[u].m, z[u].s, c);
+        }
+      }
+#pragma unroll
+      for (int d = 1; d <= 2; d <<= 1) {
+        const float m2 = __shfl_xor(M, d), s2 = __shfl_xor(S, d);
+        stat_merge(M, S, m2, s2, c);
+      }
+      M = __shfl(M, 4 * (j & 15));
+      S = __shfl(S, 4 * (j & 15));
+      const bool row_bad = j < ki && (S != S || M == -INFINITY);
       float P = -1.f;
-      if (tests)
-        P = (x >= 0 && x < vocab) ? __builtin_amdgcn_exp2f((logits[row * vocab + x] - M) * c) / S : 0.f;
-      const bool rej = tests && !(u_accept[row] < P);
+      if (tests) P = in_vocab ? __builtin_amdgcn_exp2f((lx - M) * c) / S : 0.f;
+      const bool rej = tests && !(ua < P);
       const uint64_t badm = __ballot(row_bad), rejm = __ballot(rej);
       const int a = rejm ? __ffsll((long long)rejm) - 1 : ki - 1;
       const int32_t xa = __shfl(x, a);
@@ -274,7 +295,11 @@ __global__ __launch_bounds__(kSmpThreads) void sample_finalize_kernel(
     int32_t *__restrict__ out_tokens, int32_t *status) {
   const int i = blockIdx.x;
   const int t = threadIdx.x;
+  // every load that does not depend on the request's state goes out with it
   const SampleState st = state[i];
+  const double w = t < nc2 ? wsum[(int64_t)i * nc2 + t] : 0.0;
+  const int off = offsets[i];
+  const float ud = u_draw[i];
   if (st.kind != 1) {
     if (t == 0) {
       if (st.kind == 2) status_or(status, DSV_STATUS_NAN);
@@ -290,31 +315,50 @@ __global__ __launch_bounds__(kSmpThreads) void sample_finalize_kernel(
   __shared__ int redi[kSmpThreads / kWave];
   __shared__ double sh_incl[kDrawMaxChunks], sh_w[kDrawMaxChunks];
   // locate the chunk: the first c whose inclusive prefix exceeds u * S
-  const double w = t < nc2 ? wsum[(int64_t)i * nc2 + t] : 0.0;
   const double incl = block_incl_scan_f64(w, red);
   sh_incl[t] = incl;
   sh_w[t] = w;
   __syncthreads();
   const double S = sh_incl[nc2 - 1];
-  const double target = (double)u_draw[i] * S;
+  const double target = (double)ud * S;
   // the number of chunks whose inclusive prefix is <= target (prefixes are nondecreasing)
   int cstar = block_count(t < nc2 && incl <= target, redi);
   if (cstar >= nc2) cstar = block_max_i32(t < nc2 && w > 0.0 ? t : -1, redi);
-  const int64_t row = (int64_t)offsets[i] + st.a;
+  const int64_t row = (int64_t)off + st.a;
   int32_t y = -1;
   if (cstar >= 0) {
+    // thread t owns a contiguous run of the chunk; the weights of its first kPer elements stay
+    // in registers between the sum and the search
+    constexpr int kPer = kDrawMaxChunk / kSmpThreads;
     const double tl = target - (sh_incl[cstar] - sh_w[cstar]);
     const float *x = logits + row * vocab;
     const double M = (double)__uint_as_float(st.m_bits);
     const int64_t lo = (int64_t)cstar * chunk2, hi = min(vocab, lo + chunk2);
     const int64_t per = (hi - lo + kSmpThreads - 1) / kSmpThreads;
     const int64_t a0 = min(hi, lo + t * per), a1 = min(hi, a0 + per);
+    float lv[kPer];
+    double wr[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) lv[u] = a0 + u < a1 ? x[a0 + u] : 0.f;
     double part = 0.0;
-    for (int64_t v = a0; v < a1; ++v) part += draw_weight(x[v], M, T, v, st.ex);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      wr[u] = a0 + u < a1 ? draw_weight(lv[u], M, T, a0 + u, st.ex) : 0.0;
+      part += wr[u];
+    }
+    for (int64_t v = a0 + kPer; v < a1; ++v) part += draw_weight(x[v], M, T, v, st.ex);
     const double excl = block_incl_scan_f64(part, red) - part;
     int found = INT32_MAX, last = -1;
     double cum = excl;
-    for (int64_t v = a0; v < a1; ++v) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      if (wr[u] > 0.0) {
+        last = (int)(a0 + u);
+        cum += wr[u];
+        if (found == INT32_MAX && tl < cum) found = (int)(a0 + u);
+      }
+    }
+    for (int64_t v = a0 + kPer; v < a1; ++v) {
       const double wv = draw_weight(x[v], M, T, v, st.ex);
       if (wv > 0.0) {
         last = (int)v;
@@ -331,10 +375,8 @@ __global__ __launch_bounds__(kSmpThreads) void sample_finalize_kernel(
     bonus[i] = y;
     progress[i] = 1 + a;
   }
-  if (out_tokens && t < W) {
-    const int off = offsets[i];
+  if (out_tokens && t < W)
     out_tokens[(int64_t)i * W + t] = t < a ? slot_tok[off + 1 + t] : (t == a ? y : -1);
-  }
 }
 
 // Sweep chunking: about 2048 workgroups, chunks of whole 1024-element groups (four per lane).
