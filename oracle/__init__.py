@@ -21,6 +21,8 @@ full definitions):
   first rejection draw from P without x, renormalised).
 * ``top2_margin``: the Top1-Top2 draft logit gap of DScale Fig. 4 and the
   DFlash7-ACT margin of DFlash-Mini-Lab.
+* ``draft_features``: the 18 per-position confidence values of DScale Sec. III-C
+  (Acceptance predictor).
 """
 from __future__ import annotations
 
@@ -83,6 +85,7 @@ def _load():
         lib.oracle_argmax_rows.argtypes = [i64, i64, P, P]
         lib.oracle_accept.argtypes = [i32, i32, i32] + [P] * 8
         lib.oracle_top2_margin.argtypes = [i64, i64, P, P, P]
+        lib.oracle_draft_features.argtypes = [i64, i64, P, P]
         lib.oracle_accept_sample.argtypes = [i32, i32, i32, i64, P, dbl] + [P] * 12
         lib.oracle_threads.argtypes = []
         lib.oracle_allocate.argtypes = [i32, i32, i32, i32, P, P, P]
@@ -424,3 +427,17 @@ def top2_margin(draft_logits):
     top1 = np.zeros(rows, np.int32)
     _check(lib.oracle_top2_margin(rows, vocab, _p(x), _p(margin), _p(top1)))
     return margin.reshape(lead), top1.reshape(lead)
+
+
+def draft_features(draft_logits):
+    """draft_logits [..., vocab] (vocab >= 16) -> features float32 [..., 18]: the top logit,
+    its gaps to ranks 2..16, the top token's log-probability and the entropy (DScale Sec. III-C,
+    Acceptance predictor)."""
+    lib = _load()
+    x = _c(draft_logits, np.float32)
+    lead = x.shape[:-1]
+    vocab = x.shape[-1]
+    rows = int(np.prod(lead)) if lead else 1
+    feat = np.zeros((rows, 18), np.float32)
+    _check(lib.oracle_draft_features(rows, vocab, _p(x), _p(feat)))
+    return feat.reshape(lead + (18,))

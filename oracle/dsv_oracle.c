@@ -684,6 +684,61 @@ int oracle_top2_margin(int64_t rows, int64_t vocab, const float *logits, float *
   return err;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Draft confidence features (DScale Sec. III-C "Acceptance predictor": per  */
+/* draft position, the highest logit, its gaps to ranks 2-16, the top        */
+/* token's log-probability and the entropy of the distribution; 18 values    */
+/* per position, in this order).                                              */
+/*                                                                            */
+/* For a row z of vocab >= 16 logits: sorted = z in descending order (as a   */
+/* multiset); f[0] = sorted[0]; f[r - 1] = fp32(sorted[0] - sorted[r - 1])   */
+/* for r = 2..16 (the double difference of two floats rounded once to       */
+/* float); with p = softmax(z) in double, f[16] = log p(top) and f[17] =     */
+/* -sum_{p_v > 0} p_v log p_v, each rounded to float.  A NaN or +inf logit,  */
+/* or a row with no finite logit, is an error.                                */
+/* ------------------------------------------------------------------------ */
+static int cmp_desc(const void *a, const void *b) {
+  const float x = *(const float *)a, y = *(const float *)b;
+  return x < y ? 1 : (x > y ? -1 : 0);
+}
+
+int oracle_draft_features(int64_t rows, int64_t vocab, const float *logits, float *feat) {
+  if (vocab < 16) return OR_ERR_ARG;
+  int err = OR_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < rows; ++r) {
+    const float *z = logits + r * vocab;
+    float *f = feat + r * 18;
+    int bad = 0;
+    for (int64_t v = 0; v < vocab; ++v)
+      if (isnan(z[v]) || z[v] == INFINITY) bad = 1;
+    float *sorted = malloc((size_t)vocab * sizeof(float));
+    memcpy(sorted, z, (size_t)vocab * sizeof(float));
+    if (!bad) qsort(sorted, (size_t)vocab, sizeof(float), cmp_desc);
+    if (bad || sorted[0] == -INFINITY) {
+#pragma omp atomic write
+      err = OR_ERR_NAN;
+      for (int c = 0; c < 18; ++c) f[c] = NAN;
+      free(sorted);
+      continue;
+    }
+    const double top = (double)sorted[0];
+    f[0] = sorted[0];
+    for (int rank = 2; rank <= 16; ++rank) f[rank - 1] = (float)(top - (double)sorted[rank - 1]);
+    double Z = 0.0;
+    for (int64_t v = 0; v < vocab; ++v) Z += exp((double)z[v] - top);
+    double H = 0.0;
+    for (int64_t v = 0; v < vocab; ++v) {
+      const double p = exp((double)z[v] - top) / Z;
+      if (p > 0.0) H -= p * log(p);
+    }
+    f[16] = (float)log(1.0 / Z);
+    f[17] = (float)H;
+    free(sorted);
+  }
+  return err;
+}
+
 #ifdef _OPENMP
 #include <omp.h>
 #endif
