@@ -205,6 +205,58 @@ def time_sampling(dev, copies: int, iters: int = 20):
     return res
 
 
+def time_features(dev, copies: int = 2, iters: int = 10):
+    """Draft confidence features (dsv_draft_features: top logit, gaps to ranks 2-16, top
+    log-probability, entropy per draft position) on the drafter workload's logits: 32
+    requests x 15 positions over a 248,320-token vocabulary, fp32 (476.8 MB), rotated over
+    `copies` device copies; next to the top-1/top-2 margin sweep of dsv_accept on the same
+    logits.  Device microseconds per call from HIP-graph replays of back-to-back calls, and
+    the read rate that implies."""
+    import numpy as np
+    import torch
+    import block_verification_attention_amd as dsv
+    import workloads as wl
+    x0 = torch.from_numpy(wl.draft_logits(4, 32, 248320)).to(dev)
+    xs = [x0] + [x0.clone() for _ in range(copies - 1)]
+    st = dsv.new_status(dev)
+    feat = dsv.draft_features(x0, st)
+    fws = torch.empty(max(dsv.draft_features_workspace_bytes(32 * 15, 248320), 256),
+                      dtype=torch.uint8, device=dev)
+    mo = dsv.accept(n_bs=32, W=16, status=st, draft_logits=x0)
+    mws = torch.empty(max(dsv.accept_workspace_bytes(0, 0, 32, 15, 248320), 256),
+                      dtype=torch.uint8, device=dev)
+    calls = {
+        "features_us": lambda j: dsv.draft_features(xs[j % copies], st, out=feat, workspace=fws),
+        "top2_margin_us": lambda j: dsv.accept(n_bs=32, W=16, status=st, draft_logits=xs[j % copies],
+                                               out=mo, workspace=mws),
+    }
+    res = {}
+    for name, fn in calls.items():
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for j in range(2):
+                fn(j)
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=s):
+                for j in range(iters):
+                    fn(j)
+        torch.cuda.current_stream().wait_stream(s)
+        gr.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(5):
+            gr.replay()
+        b.record()
+        torch.cuda.synchronize()
+        res[name] = a.elapsed_time(b) * 1e3 / (5 * iters)
+    nbytes = x0.numel() * 4
+    res["features_GBs"] = nbytes / (res["features_us"] * 1e-6) / 1e9
+    res["top2_margin_GBs"] = nbytes / (res["top2_margin_us"] * 1e-6) / 1e9
+    res["status"] = int(st.item())
+    return res
+
+
 def cpu_baseline(case, n_req_sample: int):
     """The oracle (pack + fp64 attention + greedy accept) on the first n_req_sample requests."""
     import numpy as np
@@ -438,6 +490,7 @@ def main():
     res["cache_map"]["scattered_GBs"] = kvb / (res["cache_map"]["scattered_us"] * 1e-6) / 1e9
     res["allocator"] = time_allocator(dev)
     res["sampling"] = time_sampling(dev, args.copies)
+    res["features"] = time_features(dev)
     if args.cpu_sample > 0:
         res["cpu_baseline"] = cpu_baseline(c, args.cpu_sample)
     print(json.dumps(res))

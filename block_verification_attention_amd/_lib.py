@@ -86,6 +86,10 @@ def load():
     lib.dsv_accept_sample_workspace_bytes.restype = ctypes.c_size_t
     lib.dsv_accept_sample.argtypes = [i32, i32, i32, i32, P, ctypes.c_float] + [P] * 11 + [ctypes.c_size_t, P, P]
     lib.dsv_accept_sample.restype = ctypes.c_int
+    lib.dsv_draft_features_workspace_bytes.argtypes = [ctypes.c_int64, i32]
+    lib.dsv_draft_features_workspace_bytes.restype = ctypes.c_size_t
+    lib.dsv_draft_features.argtypes = [ctypes.c_int64, i32, P, P, P, ctypes.c_size_t, P, P]
+    lib.dsv_draft_features.restype = ctypes.c_int
     lib.dsv_probe_stream_read.argtypes = [P, ctypes.c_size_t, P, P]
     lib.dsv_probe_stream_read.restype = ctypes.c_int
     if lib.dsv_attn_args_size() != ctypes.sizeof(AttnArgs):

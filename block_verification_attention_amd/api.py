@@ -2,7 +2,7 @@
 
 Every step runs in the HIP kernels of libdsv.so; PyTorch provides device memory and the
 stream.  Names follow the C ABI (include/dsv.h): pack_slots, allocate_pack, verify_attn,
-accept, accept_sample.
+accept, accept_sample, draft_features.
 """
 from __future__ import annotations
 
@@ -292,3 +292,33 @@ def accept_sample(*, n_bs: int, W: int, status, target_logits, temperature: floa
         _ptr(workspace), workspace.numel() if workspace is not None else 0, _ptr(status),
         _stream(stream)), "dsv_accept_sample")
     return o
+
+
+# ---------------------------------------------------------------------------
+# dsv_draft_features
+# ---------------------------------------------------------------------------
+def draft_features_workspace_bytes(rows, vocab) -> int:
+    return int(_lib.load().dsv_draft_features_workspace_bytes(rows, vocab))
+
+
+def draft_features(draft_logits, status, out=None, workspace=None, stream=None):
+    """Confidence features of draft_logits [..., vocab] (vocab >= 16): float32 [..., 18] =
+    top logit, gaps to ranks 2..16, top log-probability, entropy."""
+    lib = _lib.load()
+    dev = status.device
+    _need(draft_logits, torch.float32, "draft_logits", dev)
+    lead = tuple(draft_logits.shape[:-1])
+    vocab = draft_logits.shape[-1]
+    rows = 1
+    for n in lead:
+        rows *= n
+    if out is None:
+        out = torch.empty(lead + (18,), dtype=torch.float32, device=dev)
+    _need(out, torch.float32, "out", dev)
+    need = draft_features_workspace_bytes(rows, vocab)
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    check(lib.dsv_draft_features(rows, vocab, _ptr(draft_logits), _ptr(out), _ptr(workspace),
+                                 workspace.numel() if workspace is not None else 0, _ptr(status),
+                                 _stream(stream)), "dsv_draft_features")
+    return out

@@ -337,6 +337,34 @@ dsv_status dsv_accept_sample(int32_t n_bs, int32_t m_bs, int32_t W, int32_t voca
                              int32_t *status, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* dsv_draft_features -- per-position confidence features of the drafts      */
+/*                                                                            */
+/* DScale Sec. III-C (Acceptance predictor: every draft position contributes */
+/* its highest logit, the gaps from it to ranks 2-16, the top token's        */
+/* log-probability and the distribution's entropy, 18 values in that order). */
+/*                                                                            */
+/* draft_logits [rows][vocab] f32 (rows = requests x draft positions, in     */
+/*   draft order), vocab >= 16.  features [rows][18] f32: with the row       */
+/*   sorted descending as a multiset, f[0] = sorted[0], f[r - 1] =           */
+/*   fp32(sorted[0] - sorted[r - 1]) for r = 2..16 (exact: the rounded      */
+/*   difference), f[16] = ln softmax(row)[top] = -ln sum_v e^(z_v - top),   */
+/*   f[17] = -sum_v p_v ln p_v (fp32 accumulation; -inf logits have p = 0). */
+/*   For 15 positions a request's 270 features are features[15 i .. 15 i +  */
+/*   14], flattened.                                                          */
+/* Workspace: dsv_draft_features_workspace_bytes(rows, vocab) bytes of       */
+/*   256-byte aligned device memory, no initialisation needed.               */
+/* Errors  host: DSV_ERR_INVALID_ARG (rows < 0, vocab < 16, a missing        */
+/*   pointer, more than 2^31 workgroups), DSV_ERR_WORKSPACE.  Device: a NaN  */
+/*   or +inf logit, or a row without a finite logit, sets DSV_STATUS_NAN and */
+/*   that row's 18 features are NaN.                                          */
+/* ------------------------------------------------------------------------ */
+size_t dsv_draft_features_workspace_bytes(int64_t rows, int32_t vocab);
+
+dsv_status dsv_draft_features(int64_t rows, int32_t vocab, const float *draft_logits,
+                              float *features, void *workspace, size_t workspace_bytes,
+                              int32_t *status, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* dsv_probe_stream_read -- measurement helper (not part of the method)      */
 /*                                                                            */
 /* Reads `bytes` (rounded down to 16) of device memory at `buf` (16-byte     */

@@ -157,6 +157,11 @@ def uniforms(g, n: int) -> np.ndarray:
     return g.random(n, dtype=np.float32)
 
 
+def draft_logits(seed_config: int, n: int, vocab: int) -> np.ndarray:
+    """Draft logits [n, 15, vocab] ~ N(0,1) fp32 (one row per new draft position)."""
+    return rng(seed_config, 8).standard_normal((n, N_DRAFT_POS, vocab), dtype=np.float32)
+
+
 def make_case(
     seed_config: int,
     *,
@@ -204,8 +209,7 @@ def make_case(
     else:
         c["logits"] = None
     if draft_vocab:
-        c["draft_logits"] = rng(seed_config, 8).standard_normal((n, N_DRAFT_POS, draft_vocab),
-                                                                dtype=np.float32)
+        c["draft_logits"] = draft_logits(seed_config, n, draft_vocab)
     else:
         c["draft_logits"] = None
     c["prefill"] = None
