@@ -35,6 +35,8 @@
 
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "dsv_internal.h"
 
 namespace dsv {
@@ -367,8 +369,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     }
     map_next_base = tile_base;
   };
-  auto load_tile = [&](int tile_base, Piece (&x)[QPW]) __attribute__((always_inline)) {
-    const char *src[QPW];
+  auto tile_srcs = [&](int tile_base, const char *(&src)[QPW]) __attribute__((always_inline)) {
     if constexpr (MAP) {  // cache map: every row through its mapped pool row
       if (map_next_base != tile_base) fetch_map(tile_base);
 #pragma unroll
@@ -395,6 +396,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
         src[u] = reinterpret_cast<const char *>(r + 8 * (lane % (D / 8)));
       }
     }
+  };
+  auto load_tile = [&](int tile_base, Piece (&x)[QPW]) __attribute__((always_inline)) {
+    const char *src[QPW];
+    tile_srcs(tile_base, src);
 #pragma unroll
     for (int u = 0; u < QPW; ++u) {
       if (piece_exists(u)) {
@@ -412,6 +417,27 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
       if (piece_exists(u))
         *(lds_u32x4 *)(uintptr_t)(lds_base + stage * STAGE_BYTES + loff[u]) =
             u32x4{x[u].a, x[u].b, x[u].c, x[u].d};
+  };
+  // Stores the staged tile to LDS stage `stage` and refills each piece with the next tile's
+  // piece as soon as that piece is stored, so that the next tile's loads leave while the rest
+  // of this tile is still arriving (the scheduling barrier keeps each store-load pair in
+  // order; waits for the data are counted per piece).
+  auto store_load_tile = [&](Piece (&x)[QPW], int stage, int next_base) __attribute__((always_inline)) {
+    const char *src[QPW];
+    tile_srcs(next_base, src);
+#pragma unroll
+    for (int u = 0; u < QPW; ++u) {
+      if (piece_exists(u)) {
+        *(lds_u32x4 *)(uintptr_t)(lds_base + stage * STAGE_BYTES + loff[u]) =
+            u32x4{x[u].a, x[u].b, x[u].c, x[u].d};
+        const u32x4 v = gload_stream<u32x4>(src[u]);
+        x[u] = Piece{v[0], v[1], v[2], v[3]};
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (MAP) {
+      if (next_base + HV * TILE < t_hi) fetch_map(next_base + HV * TILE);
+    }
   };
 
   // ---- lane-constant LDS operand offsets ----
@@ -610,17 +636,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
         store_tile(xb, 1);
         if (t + 3 < n_tiles) load_tile(r_lo + (t + 3) * (HV * TILE), xb);
       } else {
-        store_tile(xa, 1);
-        if (t + 2 < n_tiles) load_tile(r_lo + (t + 2) * (HV * TILE), xa);
+        if (t + 2 < n_tiles)
+          store_load_tile(xa, 1, r_lo + (t + 2) * (HV * TILE));
+        else
+          store_tile(xa, 1);
       }
     }
     __syncthreads();
     if (t + 1 >= n_tiles) break;
     consume(r_lo + (t + 1) * (HV * TILE), std::integral_constant<int, 1>{});
     if (t + 2 < n_tiles) {
-      store_tile(xa, 0);
-      const int nxt = RSETS == 2 ? t + 4 : t + 3;
-      if (nxt < n_tiles) load_tile(r_lo + nxt * (HV * TILE), xa);
+      if constexpr (RSETS == 2) {
+        store_tile(xa, 0);
+        if (t + 4 < n_tiles) load_tile(r_lo + (t + 4) * (HV * TILE), xa);
+      } else {
+        if (t + 3 < n_tiles)
+          store_load_tile(xa, 0, r_lo + (t + 3) * (HV * TILE));
+        else
+          store_tile(xa, 0);
+      }
     }
     __syncthreads();
   }
@@ -961,8 +995,11 @@ template <> struct TileCfg<64> { static constexpr int TILE = 64; };
 template <> struct TileCfg<128> { static constexpr int TILE = 64; };
 template <> struct TileCfg<256> { static constexpr int TILE = 32; };
 
+// ev0 / ev1 (optional) are attached to the launch itself: their timestamps are the kernel's
+// start and end.
 template <int D, int NW, bool PF, int HV = 1, bool MAP = false>
-static bool launch_attn_k(const AttnParams &p, int grid, hipStream_t s) {
+static bool launch_attn_k(const AttnParams &p, int grid, hipStream_t s, hipEvent_t ev0 = nullptr,
+                          hipEvent_t ev1 = nullptr) {
   constexpr int TILE = TileCfg<D>::TILE;
   constexpr size_t shm = (size_t)2 * HV * 2 * TILE * D * sizeof(uint16_t);
   auto kern = attn_bf16_kernel<D, NW, PF, TILE, HV, MAP>;
@@ -974,40 +1011,45 @@ static bool launch_attn_k(const AttnParams &p, int grid, hipStream_t s) {
       return false;
     lds_limit_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), shm, s, p);
+  if (ev0 || ev1)
+    hipExtLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), shm, s, ev0, ev1, 0, p);
+  else
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), shm, s, p);
   return true;
 }
 
 // The cache-map variant is a separate instantiation, so that the contiguous kernel carries
 // none of its registers.
 template <int D, int NW, bool PF, int HV = 1>
-static bool launch_attn(const AttnParams &p, int grid, hipStream_t s) {
+static bool launch_attn(const AttnParams &p, int grid, hipStream_t s, hipEvent_t ev0 = nullptr,
+                        hipEvent_t ev1 = nullptr) {
   if constexpr (!PF) {
-    if (p.kv_index) return launch_attn_k<D, NW, PF, HV, true>(p, grid, s);
+    if (p.kv_index) return launch_attn_k<D, NW, PF, HV, true>(p, grid, s, ev0, ev1);
   }
-  return launch_attn_k<D, NW, PF, HV, false>(p, grid, s);
+  return launch_attn_k<D, NW, PF, HV, false>(p, grid, s, ev0, ev1);
 }
 
 template <int D>
-static int launch_verify_g(const AttnParams &p, int grid, hipStream_t s) {
+static int launch_verify_g(const AttnParams &p, int grid, hipStream_t s, hipEvent_t e0,
+                           hipEvent_t e1) {
   // groups of up to 4 heads: two KV halves (verify_halves)
   switch (p.G) {
-    case 1: return launch_attn<D, 2, false, 2>(p, grid, s);
-    case 2: return launch_attn<D, 4, false, 2>(p, grid, s);
-    case 3: return launch_attn<D, 6, false, 2>(p, grid, s);
-    case 4: return launch_attn<D, 8, false, 2>(p, grid, s);
-    case 5: return launch_attn<D, 5, false>(p, grid, s);
-    case 6: return launch_attn<D, 6, false>(p, grid, s);
-    case 7: return launch_attn<D, 7, false>(p, grid, s);
-    case 8: return launch_attn<D, 8, false>(p, grid, s);
-    case 9: return launch_attn<D, 9, false>(p, grid, s);
-    case 10: return launch_attn<D, 10, false>(p, grid, s);
-    case 11: return launch_attn<D, 11, false>(p, grid, s);
-    case 12: return launch_attn<D, 12, false>(p, grid, s);
-    case 13: return launch_attn<D, 13, false>(p, grid, s);
-    case 14: return launch_attn<D, 14, false>(p, grid, s);
-    case 15: return launch_attn<D, 15, false>(p, grid, s);
-    case 16: return launch_attn<D, 16, false>(p, grid, s);
+    case 1: return launch_attn<D, 2, false, 2>(p, grid, s, e0, e1);
+    case 2: return launch_attn<D, 4, false, 2>(p, grid, s, e0, e1);
+    case 3: return launch_attn<D, 6, false, 2>(p, grid, s, e0, e1);
+    case 4: return launch_attn<D, 8, false, 2>(p, grid, s, e0, e1);
+    case 5: return launch_attn<D, 5, false>(p, grid, s, e0, e1);
+    case 6: return launch_attn<D, 6, false>(p, grid, s, e0, e1);
+    case 7: return launch_attn<D, 7, false>(p, grid, s, e0, e1);
+    case 8: return launch_attn<D, 8, false>(p, grid, s, e0, e1);
+    case 9: return launch_attn<D, 9, false>(p, grid, s, e0, e1);
+    case 10: return launch_attn<D, 10, false>(p, grid, s, e0, e1);
+    case 11: return launch_attn<D, 11, false>(p, grid, s, e0, e1);
+    case 12: return launch_attn<D, 12, false>(p, grid, s, e0, e1);
+    case 13: return launch_attn<D, 13, false>(p, grid, s, e0, e1);
+    case 14: return launch_attn<D, 14, false>(p, grid, s, e0, e1);
+    case 15: return launch_attn<D, 15, false>(p, grid, s, e0, e1);
+    case 16: return launch_attn<D, 16, false>(p, grid, s, e0, e1);
     default: return -1;
   }
 }
@@ -1144,15 +1186,16 @@ extern "C" dsv_status dsv_verify_attn(const dsv_attn_args *a, hipStream_t stream
   }
   // ---- verification path (16-row tile) ----
   if (verify) {
-    if (a->main_begin && hipEventRecord(a->main_begin, stream) != hipSuccess) return DSV_ERR_HIP;
     if (a->dtype == DSV_BF16) {
       const int64_t grid = (int64_t)pl.n_splits * a->n_bs * a->hkv;
-      const int ok = D == 64    ? launch_verify_g<64>(p, (int)grid, stream)
-                     : D == 128 ? launch_verify_g<128>(p, (int)grid, stream)
-                                : launch_verify_g<256>(p, (int)grid, stream);
+      hipEvent_t e0 = a->main_begin, e1 = a->main_end;
+      const int ok = D == 64    ? launch_verify_g<64>(p, (int)grid, stream, e0, e1)
+                     : D == 128 ? launch_verify_g<128>(p, (int)grid, stream, e0, e1)
+                                : launch_verify_g<256>(p, (int)grid, stream, e0, e1);
       if (ok < 0) return DSV_ERR_UNSUPPORTED;
       if (ok == 0) return DSV_ERR_HIP;
     } else {
+      if (a->main_begin && hipEventRecord(a->main_begin, stream) != hipSuccess) return DSV_ERR_HIP;
       const int64_t grid = (int64_t)a->n_bs * a->W * a->hq;
       if (D == 64)
         hipLaunchKernelGGL(attn_f32_kernel<64>, dim3((unsigned)grid), dim3(256), 0, stream, p, 0);
@@ -1162,7 +1205,8 @@ extern "C" dsv_status dsv_verify_attn(const dsv_attn_args *a, hipStream_t stream
         hipLaunchKernelGGL(attn_f32_kernel<256>, dim3((unsigned)grid), dim3(256), 0, stream, p, 0);
     }
     DSV_LAUNCH_CHECK();
-    if (a->main_end && hipEventRecord(a->main_end, stream) != hipSuccess) return DSV_ERR_HIP;
+    if (a->dtype != DSV_BF16 && a->main_end && hipEventRecord(a->main_end, stream) != hipSuccess)
+      return DSV_ERR_HIP;
     if (a->dtype == DSV_BF16 && pl.n_splits > 1) {
       const int64_t rows = (int64_t)a->n_bs * a->W * a->hq;
       const int64_t grid = (rows + 256 / (D / 4) - 1) / (256 / (D / 4));

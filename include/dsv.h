@@ -226,9 +226,12 @@ typedef struct dsv_attn_args {
   size_t workspace_bytes;
   int32_t *status;
 
-  /* Optional instrumentation: when non-null, hipEventRecord is called on
-     these events on `stream` immediately before and after the verification
-     attention kernel (the split-KV merge, if any, comes after main_end). */
+  /* Optional instrumentation: when non-null, these events time the
+     verification attention kernel itself.  For bf16 they are the start and
+     stop events of its launch (hipExtLaunchKernel), so their elapsed time is
+     the kernel's duration; for fp32 they are recorded on `stream` right
+     before and after it.  The split-KV merge, if any, is not included.  Do
+     not pass them while `stream` is being captured into a graph. */
   hipEvent_t main_begin, main_end;
 
   /* Optional token-granular cache map of the verification set (the pages'
