@@ -39,9 +39,9 @@ PROFILED_KERNEL = "attn_bf16_kernel<128, 8, false, 64, 2, false>"
 # WRITE_SIZE runs (profiles/attn_verify_cfg3_hbm_traffic.md, calibrated there against the
 # streaming-read probe and a pool copy), valid for the kernel source with this SHA-256 only.
 COUNTED_SOURCE = ("block_verification_attention_amd/csrc/dsv_attn.hip",
-                  "a037a789bc1e9f38196c8b13300993bb5fed60d99ab1c30b9f455adff18b11fe")
-COUNTED_READ_BYTES = 270_556_106
-COUNTED_WRITE_BYTES = 9_461_776
+                  "0f0725c82528712261f3299960e5a38fd545432e4b865b05cee40bf14c5af676")
+COUNTED_READ_BYTES = 270_523_911
+COUNTED_WRITE_BYTES = 9_463_286
 
 
 def counted_traffic():
