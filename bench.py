@@ -257,6 +257,52 @@ def time_features(dev, copies: int = 2, iters: int = 10):
     return res
 
 
+def time_prefill(dev, iters: int = 20):
+    """Prefill attention with the 128-row wide tile (row a6; bf16 MFMA-bound) on the mixed
+    workload's prefill set: 4 fresh requests of 4096 causal rows (context 0), 32 query / 8 KV
+    heads, head_dim 128, seeded N(0,1) * 0.5 inputs made on the device.  Work per call:
+    sum over rows of the visible keys x 32 heads x 128 x 4 flop (Q.K and P.V) = 5.50e11
+    flop.  Device time per call from HIP events around each dsv_verify_attn call (prefill
+    only, the pool already holding the rows' K/V), median of `iters`, against the dense bf16
+    MFMA peak of 2.5 PFLOP/s."""
+    import numpy as np
+    import torch
+    import block_verification_attention_amd as dsv
+    n_req, q_len, hq, hkv, d = 4, 4096, 32, 8, 128
+    g = torch.Generator(device=dev)
+    g.manual_seed(5005)
+    rows = n_req * q_len
+    kp = (torch.randn((hkv, rows, d), generator=g, device=dev) * 0.5).to(torch.bfloat16)
+    vp = (torch.randn((hkv, rows, d), generator=g, device=dev) * 0.5).to(torch.bfloat16)
+    q = (torch.randn((rows, hq, d), generator=g, device=dev) * 0.5).to(torch.bfloat16)
+    i32 = lambda a: torch.tensor(a, dtype=torch.int32, device=dev)  # noqa: E731
+    pf = dsv.Prefill(q_start=i32([r * q_len for r in range(n_req)]), q_len=i32([q_len] * n_req),
+                     ctx_len=i32([0] * n_req),
+                     kv_base=torch.tensor([r * q_len for r in range(n_req)], dtype=torch.int64, device=dev),
+                     q=q, out=torch.empty_like(q), max_len=q_len,
+                     lse=torch.empty((rows, hq), dtype=torch.float32, device=dev))
+    st = dsv.new_status(dev)
+    args = dsv.attn_args(None, kp, vp, None, None, None, None, W=16, max_ctx=0, out=None, status=st,
+                         prefill=pf)
+    for _ in range(3):
+        dsv.verify_attn_call(args)
+    evs = []
+    for _ in range(iters):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dsv.verify_attn_call(args)
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3
+    flop = 4.0 * hq * d * n_req * q_len * (q_len + 1) / 2
+    tflops = flop / (us * 1e-6) / 1e12
+    return {"workload": "prefill, 4 x 4096 causal rows, 32/8 heads, head_dim 128, bf16",
+            "kernel": "attn_bf16_kernel<128, 8, true, 64, 1, false>", "us": us, "flop": flop,
+            "TFLOPs": tflops, "peak_TFLOPs": 2500.0, "frac": tflops / 2500.0,
+            "status": int(st.item())}
+
+
 def cpu_baseline(case, n_req_sample: int):
     """The oracle (pack + fp64 attention + greedy accept) on the first n_req_sample requests."""
     import numpy as np
@@ -491,6 +537,7 @@ def main():
     res["allocator"] = time_allocator(dev)
     res["sampling"] = time_sampling(dev, args.copies)
     res["features"] = time_features(dev)
+    res["prefill"] = time_prefill(dev)
     if args.cpu_sample > 0:
         res["cpu_baseline"] = cpu_baseline(c, args.cpu_sample)
     print(json.dumps(res))
