@@ -303,6 +303,68 @@ def time_prefill(dev, iters: int = 20):
             "status": int(st.item())}
 
 
+def time_other_verify(dev, ev, iters: int = 20):
+    """Verification attention on the two other verification shapes of the configuration set,
+    with their seeded prefix lengths and contexts and seeded N(0,1) * 0.5 device-made K/V:
+    32 requests sharing 256 slots at contexts U[4096, 8192], 24 query / 2 KV heads, head_dim
+    256 (12 query heads per KV head); and 60 requests sharing 480 slots at contexts
+    U[8192, 32768], 32 / 8 heads, head_dim 128.  Kernel time from the start/stop events
+    attached to the verification kernel's launch (median of `iters`), algorithmic KV bytes
+    (every visible K and V row once) over it, against 8 TB/s."""
+    import numpy as np
+    import torch
+    import block_verification_attention_amd as dsv
+    import workloads as wl
+    out = {}
+    shapes = {
+        "32x256_slots_ctx4k-8k_24q2kv_d256": (4, 32, 256, 4096, 8193, 24, 2, 256, 2),
+        "60x480_slots_ctx8k-32k_32q8kv_d128": (5, 60, 480, 8192, 32769, 32, 8, 128, 1),
+    }
+    for name, (cfg, n, m_bs, lo, hi, hq, hkv, d, copies) in shapes.items():
+        g = wl.rng(cfg, 0)
+        k = wl.lengths_geometric_rescaled(g, n, m_bs)
+        ctx = g.integers(lo, hi, size=n).astype(np.int32)
+        seg = (ctx + 16).astype(np.int64)
+        base = np.concatenate([[0], np.cumsum(seg)[:-1]]).astype(np.int64)
+        rows = int(seg.sum())
+        tg = torch.Generator(device=dev)
+        tg.manual_seed(7000 + cfg)
+        pools = [((torch.randn((hkv, rows, d), generator=tg, device=dev) * 0.5).to(torch.bfloat16),
+                  (torch.randn((hkv, rows, d), generator=tg, device=dev) * 0.5).to(torch.bfloat16))
+                 for _ in range(copies)]
+        q = (torch.randn((m_bs, hq, d), generator=tg, device=dev) * 0.5).to(torch.bfloat16)
+        kn = (torch.randn((m_bs, hkv, d), generator=tg, device=dev) * 0.5).to(torch.bfloat16)
+        vn = (torch.randn((m_bs, hkv, d), generator=tg, device=dev) * 0.5).to(torch.bfloat16)
+        kd, cd, bd = (torch.from_numpy(a).to(dev) for a in (k, ctx, base))
+        tok = torch.zeros((n, 16), dtype=torch.int32, device=dev)
+        st = dsv.new_status(dev)
+        packed = dsv.pack_slots(kd, cd, bd, tok, m_bs, st)
+        o = torch.empty_like(q)
+        lse = torch.empty((m_bs, hq), dtype=torch.float32, device=dev)
+        evs = ev.create(2 * iters)
+        args = [dsv.attn_args(q, *pools[j % copies], packed["offsets"], kd, cd, bd, W=16,
+                              max_ctx=int(ctx.max()), out=o, status=st, lse=lse, k_new=kn, v_new=vn,
+                              slot_cache_loc=packed["slot_cache_loc"],
+                              events=(evs[2 * j].value, evs[2 * j + 1].value)) for j in range(iters)]
+        ws = torch.empty(max(dsv.verify_attn_workspace_bytes(args[0]), 256), dtype=torch.uint8, device=dev)
+        for a in args:
+            a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+        for j in range(3):
+            dsv.verify_attn_call(args[j])
+        torch.cuda.synchronize()
+        for a in args:
+            dsv.verify_attn_call(a)
+        torch.cuda.synchronize()
+        us = float(np.median([ev.elapsed_ms(evs[2 * j], evs[2 * j + 1]) for j in range(iters)])) * 1e3
+        ev.destroy(evs)
+        kvb = int(((ctx.astype(np.int64) + k) * hkv * d * 2 * 2).sum())
+        out[name] = {"kernel_us": us, "algorithmic_bytes": kvb, "GBs": kvb / (us * 1e-6) / 1e9,
+                     "frac": kvb / (us * 1e-6) / 8e12, "slots": int(k.sum()), "status": int(st.item())}
+        del pools, args
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(case, n_req_sample: int):
     """The oracle (pack + fp64 attention + greedy accept) on the first n_req_sample requests."""
     import numpy as np
@@ -538,6 +600,7 @@ def main():
     res["sampling"] = time_sampling(dev, args.copies)
     res["features"] = time_features(dev)
     res["prefill"] = time_prefill(dev)
+    res["other_verify"] = time_other_verify(dev, ev)
     if args.cpu_sample > 0:
         res["cpu_baseline"] = cpu_baseline(c, args.cpu_sample)
     print(json.dumps(res))

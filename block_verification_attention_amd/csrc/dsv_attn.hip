@@ -52,6 +52,7 @@ struct AttnParams {
   void *k_pool, *v_pool;
   int64_t pool_rows, stride_head, stride_row;
   int hq, hkv, G;
+  int GW, HG;        // verification: query heads per workgroup, head groups per KV head
   float scale;       // softmax scale
   float scale_log2;  // softmax scale * log2(e)
   // verification set
@@ -229,7 +230,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
   const int wh = HV == 1 ? w : w - half * NWH;
 
   // ---- work unit ----
-  int g, h, c, r_lo, r_hi, row0, nrows, split = 0, n_splits_i = 1, off = 0;
+  int g, h, c, r_lo, r_hi, row0, nrows, split = 0, n_splits_i = 1, off = 0, hg = 0;
   int64_t kb, q_row0;
   const uint16_t *qsrc;
   const uint16_t *knew = nullptr, *vnew = nullptr;
@@ -237,24 +238,27 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
   if constexpr (!PF) {
     const int bid = blockIdx.x;
     g = bid % p.hkv;
-    const int t = bid / p.hkv;
+    const int t0 = bid / p.hkv;
+    hg = t0 % p.HG;  // this workgroup's query heads: [G g + GW hg, + GW)
+    const int t = t0 / p.HG;
     const int i = t % p.n_bs;
     split = t / p.n_bs;
-    h = g * p.G + wh;
+    const int h0 = g * p.G + hg * p.GW;
+    h = h0 + wh;
     if (i == 0 && split == 0) {
       int end = p.offsets[p.n_bs];
       end = end < 0 ? 0 : (end > p.m_bs ? p.m_bs : end);
-      zero_rows_bf16<D>(static_cast<uint16_t *>(p.out), p.lse, p.hq, end, p.m_bs, g * p.G, p.G,
+      zero_rows_bf16<D>(static_cast<uint16_t *>(p.out), p.lse, p.hq, end, p.m_bs, h0, p.GW,
                         tid, NW * 64);
     }
     int ki;
     const int bad = verify_request(p, i, ki, off, c, kb);
     if (bad) {
       if (split == 0) {
-        if (tid == 0 && g == 0) status_or(p.status, bad);
+        if (tid == 0 && g == 0 && hg == 0) status_or(p.status, bad);
         if (ki >= 0 && ki <= p.W && off >= 0 && (int64_t)off + ki <= p.m_bs)
-          zero_rows_bf16<D>(static_cast<uint16_t *>(p.out), p.lse, p.hq, off, off + ki, g * p.G,
-                            p.G, tid, NW * 64);
+          zero_rows_bf16<D>(static_cast<uint16_t *>(p.out), p.lse, p.hq, off, off + ki, h0,
+                            p.GW, tid, NW * 64);
       }
       return;
     }
@@ -663,7 +667,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     // This step's KV writes, by split 0 of each (request, KV head) after its tile loop, so that
     // they stay off the critical path (the kernel reads candidates from k_new, not from the
     // pool): candidate j goes to pool row slot_cache_loc[off + j].
-    if (knew && split == 0) {
+    if (knew && split == 0 && hg == 0) {
       constexpr int C16 = D / 8;
       for (int e = tid; e < nrows * C16 * 2; e += NW * 64) {
         const int isv = e / (nrows * C16);
@@ -957,6 +961,21 @@ struct Plan {
 // G waves each (one 8-wave workgroup per CU for G = 4), larger groups one.
 static int verify_halves(int G) { return G <= 4 ? 2 : 1; }
 
+// Query heads per verification workgroup.  One wave per head keeps a head's output
+// accumulators (D / 4 registers per lane) in its own registers; for head_dim 256 a group of
+// more than four heads in one workgroup does not fit the register budget of its occupancy
+// (it spills heavily), so the group's heads are spread over G / GW workgroups, which each
+// read the KV head's rows: GW = the largest divisor of G not above 4 (measured on 12 heads
+// per KV head: 6 heads per workgroup 1077 us, 4 heads 554 us, 3 heads 1366 us, 2 heads 607
+// us for the same 402 MB of KV).
+static int verify_heads_per_wg(int D, int G) {
+  if (D >= 256 && G > 4) {
+    for (int gw = 4; gw > 1; --gw)
+      if (G % gw == 0) return gw;
+  }
+  return G;
+}
+
 // Split plan of the verification set: KV rows per split (multiple of 64) and the most splits
 // per request the grid provides.  Auto: aim for 512 wave groups (G waves, one per query head
 // of the group) in flight, two per SIMD on 256 CUs: 512 single-half or 256 two-half
@@ -971,8 +990,10 @@ static Plan make_plan(const dsv_attn_args *a) {
   const int64_t rows = (int64_t)a->max_ctx + a->W;
   int64_t chunk = a->kv_chunk;
   if (chunk <= 0) {
-    const int64_t units = (int64_t)a->n_bs * a->hkv;
-    const int64_t wgs = 512 / verify_halves(a->hkv > 0 ? a->hq / a->hkv : 1);
+    const int G = a->hkv > 0 ? a->hq / a->hkv : 1;
+    const int GW = verify_heads_per_wg(a->d, G);
+    const int64_t units = (int64_t)a->n_bs * a->hkv * (G / GW);
+    const int64_t wgs = 512 / verify_halves(GW);
     int64_t target = (wgs + units - 1) / units;
     if (target < 1) target = 1;
     if (target > 64) target = 64;
@@ -1033,7 +1054,7 @@ template <int D>
 static int launch_verify_g(const AttnParams &p, int grid, hipStream_t s, hipEvent_t e0,
                            hipEvent_t e1) {
   // groups of up to 4 heads: two KV halves (verify_halves)
-  switch (p.G) {
+  switch (p.GW) {
     case 1: return launch_attn<D, 2, false, 2>(p, grid, s, e0, e1);
     case 2: return launch_attn<D, 4, false, 2>(p, grid, s, e0, e1);
     case 3: return launch_attn<D, 6, false, 2>(p, grid, s, e0, e1);
@@ -1117,6 +1138,8 @@ extern "C" dsv_status dsv_verify_attn(const dsv_attn_args *a, hipStream_t stream
   p.hq = a->hq;
   p.hkv = a->hkv;
   p.G = G;
+  p.GW = verify_heads_per_wg(a->d, G);
+  p.HG = G / p.GW;
   p.scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.0f / sqrtf((float)a->d);
   p.scale_log2 = p.scale * 1.4426950408889634f;
   p.n_bs = a->n_bs;
@@ -1187,7 +1210,7 @@ extern "C" dsv_status dsv_verify_attn(const dsv_attn_args *a, hipStream_t stream
   // ---- verification path (16-row tile) ----
   if (verify) {
     if (a->dtype == DSV_BF16) {
-      const int64_t grid = (int64_t)pl.n_splits * a->n_bs * a->hkv;
+      const int64_t grid = (int64_t)pl.n_splits * a->n_bs * a->hkv * p.HG;
       hipEvent_t e0 = a->main_begin, e1 = a->main_end;
       const int ok = D == 64    ? launch_verify_g<64>(p, (int)grid, stream, e0, e1)
                      : D == 128 ? launch_verify_g<128>(p, (int)grid, stream, e0, e1)
