@@ -34,7 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-PROFILED_KERNEL = "attn_bf16_kernel<128, 8, false, 64, 2, false>"
+PROFILED_KERNEL = "attn_bf16_kernel<128, 8, false, 64, 2, false, 1>"
 # HBM bytes per launch of that kernel on this workload, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs (profiles/attn_verify_cfg3_hbm_traffic.md, calibrated there against the
 # streaming-read probe and a pool copy), valid for the kernel source with this SHA-256 only.
