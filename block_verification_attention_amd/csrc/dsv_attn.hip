@@ -980,12 +980,18 @@ constexpr int kWideHeadsPerWg = DSV_WIDE_HEADS_PER_WG;
 // state at two or three waves per SIMD, so each head gets two waves that split the output
 // columns (verify_waves_per_head), and a KV head's query heads are spread over G / GW
 // workgroups of 2 GW waves, which each read the KV head's rows: GW = the largest divisor of
-// G not above kWideHeadsPerWg.  Other head dims keep the whole group in one workgroup.
+// G not above kWideHeadsPerWg.  Head_dim 128 keeps groups of up to 8 heads whole.
 static int verify_heads_per_wg(int D, int G) {
   if (D >= 256) {
     for (int gw = kWideHeadsPerWg; gw > 1; --gw)
       if (G % gw == 0) return gw;
     return 1;
+  }
+  // head_dim 128: more than 8 one-head waves per workgroup run at 3-4 waves per SIMD and
+  // spill; split the group into workgroups of at most 8 heads when G has such a divisor
+  if (D >= 128 && G > 8) {
+    for (int gw = 8; gw > 1; --gw)
+      if (G % gw == 0) return gw;
   }
   return G;
 }
