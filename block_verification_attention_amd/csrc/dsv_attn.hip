@@ -42,6 +42,7 @@
 namespace dsv {
 
 constexpr int kTileKV = 64;  // split granularity (multiple of every tile height)
+constexpr int kXcds = 8;     // dispatch places block b on XCD b % 8
 // Waves with at most this many 16-byte loads per tile stage two tiles in registers (more
 // would push the hot shapes past the register budget of two waves per SIMD).
 constexpr int kTwoSetMaxLoads = 4;
@@ -53,6 +54,8 @@ struct AttnParams {
   int64_t pool_rows, stride_head, stride_row;
   int hq, hkv, G;
   int GW, HG;        // verification: query heads per workgroup, head groups per KV head
+  int xcd_sib_v;     // verification: HG sibling workgroups share an XCD (0: plain order)
+  int xcd_sib_pf;    // prefill: the G query heads of a KV head share an XCD (0: plain order)
   float scale;       // softmax scale
   float scale_log2;  // softmax scale * log2(e)
   // verification set
@@ -242,11 +245,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
   const uint16_t *knew = nullptr, *vnew = nullptr;
   const int32_t *kvi = nullptr;  // the request's cache-map row (verification with a cache map)
   if constexpr (!PF) {
-    const int bid = blockIdx.x;
-    g = bid % p.hkv;
-    const int t0 = bid / p.hkv;
-    hg = t0 % p.HG;  // this workgroup's query heads: [G g + GW hg, + GW)
-    const int t = t0 / p.HG;
+    // Workgroups that read the same KV rows (the HG head groups of a (request, KV head,
+    // split)) are consecutive blocks on one XCD, so that they run together and share its L2:
+    // blocks go to XCD b % 8, so siblings are b, b + 8, ... (grid a multiple of 8 HG).
+    int bid = blockIdx.x, t0;
+    if (p.xcd_sib_v) {
+      const int slot = bid / kXcds;
+      hg = slot % p.HG;
+      const int u = (slot / p.HG) * kXcds + bid % kXcds;
+      g = u % p.hkv;
+      t0 = u / p.hkv;
+    } else {
+      g = bid % p.hkv;
+      t0 = bid / p.hkv;
+      hg = t0 % p.HG;  // this workgroup's query heads: [G g + GW hg, + GW)
+      t0 /= p.HG;
+    }
+    const int t = t0;
     const int i = t % p.n_bs;
     split = t / p.n_bs;
     const int h0 = g * p.G + hg * p.GW;
@@ -283,12 +298,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
       vnew = static_cast<const uint16_t *>(p.v_new);
     }
   } else {
-    const int bid = blockIdx.x;
-    const int per = p.n_pf * p.hq;
-    const int b = p.pf_blocks - 1 - bid / per;  // longest row blocks first
-    const int r = (bid % per) / p.hq;
-    h = (bid % per) % p.hq;
-    g = h / p.G;
+    // The G query heads of a (request, KV head, row block) read the same KV tiles: with
+    // xcd_sib_pf they are consecutive blocks on one XCD (grid a multiple of 8 G).
+    int bid = blockIdx.x, b, r;
+    if (p.xcd_sib_pf) {
+      const int slot = bid / kXcds;
+      const int hig = slot % p.G;
+      const int u = (slot / p.G) * kXcds + bid % kXcds;  // (row block, request, KV head)
+      const int per_u = p.n_pf * p.hkv;
+      b = p.pf_blocks - 1 - u / per_u;  // longest row blocks first
+      r = (u % per_u) / p.hkv;
+      g = u % p.hkv;
+      h = g * p.G + hig;
+    } else {
+      const int per = p.n_pf * p.hq;
+      b = p.pf_blocks - 1 - bid / per;  // longest row blocks first
+      r = (bid % per) / p.hq;
+      h = (bid % per) % p.hq;
+      g = h / p.G;
+    }
     int ql, qs;
     const int bad = prefill_request(p, r, ql, qs, c, kb);
     if (bad) {
@@ -1237,6 +1265,7 @@ extern "C" dsv_status dsv_verify_attn(const dsv_attn_args *a, hipStream_t stream
     }
     if (a->dtype == DSV_BF16) {
       const int grid = (int)((int64_t)p.pf_blocks * a->n_pf * a->hq);
+      p.xcd_sib_pf = p.G > 1 && grid % (kXcds * p.G) == 0;
       const bool ok = D == 64    ? launch_attn<64, kPfWaves, true>(p, grid, stream)
                       : D == 128 ? launch_attn<128, kPfWaves, true>(p, grid, stream)
                                  : launch_attn<256, kPfWaves, true>(p, grid, stream);
@@ -1256,6 +1285,7 @@ extern "C" dsv_status dsv_verify_attn(const dsv_attn_args *a, hipStream_t stream
   if (verify) {
     if (a->dtype == DSV_BF16) {
       const int64_t grid = (int64_t)pl.n_splits * a->n_bs * a->hkv * p.HG;
+      p.xcd_sib_v = p.HG > 1 && grid % (kXcds * p.HG) == 0;
       hipEvent_t e0 = a->main_begin, e1 = a->main_end;
       const int ok = D == 64    ? launch_verify_g<64>(p, (int)grid, stream, e0, e1)
                      : D == 128 ? launch_verify_g<128>(p, (int)grid, stream, e0, e1)
