@@ -39,9 +39,9 @@ PROFILED_KERNEL = "attn_bf16_kernel<128, 8, false, 64, 2, false, 1>"
 # WRITE_SIZE runs (profiles/attn_verify_cfg3_hbm_traffic.md, calibrated there against the
 # streaming-read probe and a pool copy), valid for the kernel source with this SHA-256 only.
 COUNTED_SOURCE = ("block_verification_attention_amd/csrc/dsv_attn.hip",
-                  "0f0725c82528712261f3299960e5a38fd545432e4b865b05cee40bf14c5af676")
-COUNTED_READ_BYTES = 270_523_911
-COUNTED_WRITE_BYTES = 9_463_286
+                  "9c73ed1d3eb711731debce0f8959cc09ef201dcd60204b6975f5048b922a350c")
+COUNTED_READ_BYTES = 270_569_711
+COUNTED_WRITE_BYTES = 9_470_116
 
 
 def counted_traffic():
