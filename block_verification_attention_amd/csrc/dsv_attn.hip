@@ -1048,8 +1048,10 @@ static Plan make_plan(const dsv_attn_args *a) {
     const int GW = verify_heads_per_wg(a->d, G);
     const int64_t units = (int64_t)a->n_bs * a->hkv * (G / GW);
     // wave groups in flight: two per SIMD (512 groups of G waves, or 256 two-half ones); the
-    // wide-head workgroups (2 GW waves) aim at one per CU
-    const int64_t wgs = verify_waves_per_head(a->d) == 2 ? 256 : 512 / verify_halves(GW);
+    // wide-head workgroups (2 GW waves, one per CU at a time) aim at four rounds, whose
+    // shorter splits balance requests of different lengths (32 requests at 4k-8k with 12
+    // heads per KV head: 270 us at two splits, 247-264 us at 512-1344-row splits)
+    const int64_t wgs = verify_waves_per_head(a->d) == 2 ? 1024 : 512 / verify_halves(GW);
     int64_t target = (wgs + units - 1) / units;
     if (target < 1) target = 1;
     if (target > 64) target = 64;
@@ -1082,7 +1084,10 @@ template <> struct TileCfg<256> { static constexpr int TILE = 32; };
 template <int D, int NW, bool PF, int HV = 1, bool MAP = false, int DS = 1>
 static bool launch_attn_k(const AttnParams &p, int grid, hipStream_t s, hipEvent_t ev0 = nullptr,
                           hipEvent_t ev1 = nullptr) {
-  constexpr int TILE = TileCfg<D>::TILE;
+  // the two-waves-per-head verification kernel takes 64-row tiles when a tile's wave loads
+  // split evenly over its waves (fewer, longer stages; otherwise the uneven piece pattern
+  // spills)
+  constexpr int TILE = (DS > 1 && (64 / (1024 / (2 * D))) % NW == 0) ? 64 : TileCfg<D>::TILE;
   constexpr size_t shm = (size_t)2 * HV * 2 * TILE * D * sizeof(uint16_t);
   auto kern = attn_bf16_kernel<D, NW, PF, TILE, HV, MAP, DS>;
   // once per kernel (idempotent), so that a captured call contains launches only
