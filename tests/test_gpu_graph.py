@@ -1,0 +1,103 @@
+"""HIP-graph capture of the calls beyond the greedy step: budget allocator + pack, verification
+attention through a cache map, a head_dim-256 launch with head groups and two waves per head,
+the sampling-mode verifier and the draft confidence features.  One captured graph holds all
+of them; three replays, with eager work and synchronisation between them, reproduce the eager
+outputs bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+import workloads as wl  # noqa: E402
+from gpu_util import DEV, device_case, gpu_pack, small_case, to_dev  # noqa: E402
+import block_verification_attention_amd as dsv  # noqa: E402
+
+
+def test_next_rows_graph_capture_replays_match_eager():
+    g = np.random.default_rng(90)
+    st = dsv.new_status(DEV)
+    # budget allocator fused with the packer
+    n_bs = 12
+    scores = to_dev(g.random((n_bs, 15), dtype=np.float32))
+    actx = to_dev(g.integers(0, 500, n_bs).astype(np.int32))
+    abase = to_dev((np.arange(n_bs) * 600).astype(np.int64))
+    atok = to_dev(g.integers(0, 1000, (n_bs, 16)).astype(np.int32))
+    alloc = dsv.allocate_pack(scores, 10, 80, actx, abase, atok, 96, st)
+    # cache-map verification (identity map over contiguous segments)
+    c = small_case(91, hq=8, hkv=2, d=128, k=(16, 9, 1, 12), ctx=(700, 1300, 5, 260))
+    d = device_case(c)
+    packed = gpu_pack(c, d)
+    stride = int((c["ctx_len"] + c["k"]).max())
+    idx = np.minimum(c["kv_base"][:, None] + np.arange(stride)[None, :], c["k_pool"].shape[1] - 1)
+    kv_index = to_dev(idx.astype(np.int32))
+    out = torch.zeros_like(d["q"])
+    lse = torch.zeros((c["m_bs"], c["hq"]), device=DEV)
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device=DEV)
+    # head_dim 256, 6 query heads per KV head (head groups of 3, two waves per head)
+    c2 = small_case(92, hq=12, hkv=2, d=256, k=(16, 3, 9), ctx=(900, 40, 2100))
+    d2 = device_case(c2)
+    packed2 = gpu_pack(c2, d2)
+    out2 = torch.zeros_like(d2["q"])
+    lse2 = torch.zeros((c2["m_bs"], c2["hq"]), device=DEV)
+    ws2 = torch.zeros(1 << 22, dtype=torch.uint8, device=DEV)
+    # sampling-mode verifier
+    sk = np.array([16, 5, 0, 11], np.int32)
+    slog, sbt = wl.sampling_logits(g, sk, 3000, int(sk.sum()) + 2, g.integers(0, 3000, (4, 16)).astype(np.int32),
+                                   boost=(0.0, 8.0))
+    sp = dsv.pack_slots(to_dev(sk), to_dev(np.zeros(4, np.int32)), to_dev(np.zeros(4, np.int64)),
+                        to_dev(sbt), int(sk.sum()) + 2, st)
+    slogits = to_dev(slog)
+    u_acc = to_dev(wl.uniforms(g, slog.shape[0]))
+    u_draw = to_dev(wl.uniforms(g, 4))
+    skd = to_dev(sk)
+    sws = torch.zeros(dsv.accept_sample_workspace_bytes(4, slog.shape[0], 3000), dtype=torch.uint8, device=DEV)
+    sout = {}
+    # draft features
+    dl = to_dev(g.standard_normal((3, 15, 4096), dtype=np.float32))
+    fout = torch.zeros((3, 15, 18), dtype=torch.float32, device=DEV)
+    fws = torch.zeros(dsv.draft_features_workspace_bytes(45, 4096), dtype=torch.uint8, device=DEV)
+
+    def calls():
+        dsv.allocate_pack(scores, 10, 80, actx, abase, atok, 96, st, out=alloc)
+        a = dsv.attn_args(d["q"], d["k_pool"], d["v_pool"], packed["offsets"], d["k"], d["ctx_len"],
+                          d["kv_base"], W=16, max_ctx=1300, out=out, status=st, lse=lse,
+                          k_new=d["k_new"], v_new=d["v_new"], slot_cache_loc=packed["slot_cache_loc"],
+                          workspace=ws, kv_index=kv_index)
+        dsv.verify_attn_call(a)
+        a2 = dsv.attn_args(d2["q"], d2["k_pool"], d2["v_pool"], packed2["offsets"], d2["k"], d2["ctx_len"],
+                           d2["kv_base"], W=16, max_ctx=2100, out=out2, status=st, lse=lse2,
+                           k_new=d2["k_new"], v_new=d2["v_new"], slot_cache_loc=packed2["slot_cache_loc"],
+                           kv_chunk=256, workspace=ws2)
+        dsv.verify_attn_call(a2)
+        dsv.accept_sample(n_bs=4, W=16, status=st, target_logits=slogits, temperature=0.8,
+                          slot_tok=sp["slot_tok"], offsets=sp["offsets"], k=skd, u_accept=u_acc,
+                          u_draw=u_draw, out=sout, workspace=sws)
+        dsv.draft_features(dl, st, out=fout, workspace=fws)
+
+    calls()
+    torch.cuda.synchronize()
+    results = lambda: [alloc[k] for k in sorted(alloc)] + [out, lse, out2, lse2] + \
+        [sout[k] for k in sorted(sout)] + [fout]  # noqa: E731
+    eager = [t.clone() for t in results()]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    for r in range(3):
+        for t in results():
+            if t.dtype in (torch.float32, torch.bfloat16):
+                t.fill_(float("nan"))
+            else:
+                t.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for j, (t, e) in enumerate(zip(results(), eager)):
+            if t.dtype == torch.bfloat16:
+                ok = torch.equal(t.view(torch.int16), e.view(torch.int16))
+            elif t.dtype == torch.float32:
+                ok = torch.equal(t.view(torch.int32), e.view(torch.int32))
+            else:
+                ok = torch.equal(t, e)
+            assert ok, f"replay {r}, output {j}"
+    assert int(st.item()) == 0
