@@ -29,6 +29,29 @@ __device__ __forceinline__ int64_t wave_inclusive_scan(int64_t v, int lane) {
 // One workgroup of NT threads (a multiple of 64, at most 1024).  Thread t owns the contiguous
 // run of requests [t * per, (t + 1) * per); the per-thread sums are scanned with wavefront
 // scans and one cross-wave pass, so the scan costs two barriers.
+// Writes the slots [off, off + k) of request i (k <= W <= DSV_MAX_W): the request's tokens
+// are loaded together first, so the writes wait for one memory round trip, not one per slot.
+__device__ __forceinline__ void write_request_slots(int i, int k, int off, int W, int c, int64_t kb,
+                                                    const int32_t *__restrict__ block_tokens,
+                                                    int32_t *__restrict__ slot_req,
+                                                    int32_t *__restrict__ slot_tok,
+                                                    int32_t *__restrict__ slot_pos,
+                                                    int64_t *__restrict__ slot_cache_loc) {
+  int32_t tok[DSV_MAX_W];
+#pragma unroll
+  for (int j = 0; j < DSV_MAX_W; ++j) tok[j] = j < k ? block_tokens[(int64_t)i * W + j] : 0;
+#pragma unroll
+  for (int j = 0; j < DSV_MAX_W; ++j) {
+    if (j < k) {
+      const int s = off + j;
+      slot_req[s] = i;
+      slot_tok[s] = tok[j];
+      slot_pos[s] = c + j;
+      slot_cache_loc[s] = kb + c + j;
+    }
+  }
+}
+
 __global__ __launch_bounds__(kPackMaxThreads) void pack_slots_kernel(
     int n_bs, int W, int m_bs, const int32_t *__restrict__ k, const int32_t *__restrict__ ctx_len,
     const int64_t *__restrict__ kv_base, const int32_t *__restrict__ block_tokens,
@@ -70,15 +93,8 @@ __global__ __launch_bounds__(kPackMaxThreads) void pack_slots_kernel(
     offsets[i] = (int32_t)run;
     int ki = drop_all ? 0 : eff(i);
     int base = (int)run;
-    int c = ctx_len[i];
-    int64_t kb = kv_base[i];
-    for (int j = 0; j < ki; ++j) {
-      int s = base + j;
-      slot_req[s] = i;
-      slot_tok[s] = block_tokens[(int64_t)i * W + j];
-      slot_pos[s] = c + j;
-      slot_cache_loc[s] = kb + c + j;
-    }
+    write_request_slots(i, ki, base, W, ctx_len[i], kv_base[i], block_tokens, slot_req, slot_tok,
+                        slot_pos, slot_cache_loc);
     run += ki;
   }
   const int end = drop_all ? 0 : (int)total;
@@ -245,15 +261,8 @@ __global__ __launch_bounds__(kAllocMaxRequests) void allocate_pack_kernel(
     if (k0_out) k0_out[i] = k0;
     offsets[i] = fits ? off : 0;
     if (fits) {
-      const int c = ctx_len[i];
-      const int64_t kb = kv_base[i];
-      for (int j = 0; j < k; ++j) {
-        const int s = off + j;
-        slot_req[s] = i;
-        slot_tok[s] = block_tokens[(int64_t)i * W + j];
-        slot_pos[s] = c + j;
-        slot_cache_loc[s] = kb + c + j;
-      }
+      write_request_slots(i, k, off, W, ctx_len[i], kv_base[i], block_tokens, slot_req, slot_tok,
+                          slot_pos, slot_cache_loc);
     }
   }
   const int tail = fits ? end : 0;
