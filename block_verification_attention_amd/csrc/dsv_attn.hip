@@ -804,21 +804,32 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   if (S <= 1) return;
   const int64_t plane = (int64_t)p.m_bs * p.hq;
   const int64_t rh = (int64_t)(off + j) * p.hq + h;
-  // one pass with a running maximum; the loads of up to eight splits are issued together
+  // one pass with a running maximum over the splits in order; the loads of eight splits at a
+  // time are all issued before any is combined
   float M = -INFINITY, den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
   const f32x4 *src = reinterpret_cast<const f32x4 *>(p.ws_o + rh * D) + l4;
   const int64_t step4 = plane * D / 4;
-#pragma unroll 8
-  for (int s = 0; s < S; ++s) {
-    const float ls = gload<float>(p.ws_lse + s * plane + rh);
-    const f32x4 o = gload<f32x4>(src + s * step4);
-    const float m_new = fmaxf(M, ls);
-    const float a = m_new == -INFINITY ? 1.f : __expf(M - m_new);   // rescale of the sum so far
-    const float b = ls == -INFINITY ? 0.f : __expf(ls - m_new);     // weight of split s
-    den = den * a + b;
-    num = num * a + b * o;
-    M = m_new;
+  constexpr int kBatch = 8;
+  for (int s0 = 0; s0 < S; s0 += kBatch) {
+    float ls[kBatch];
+    f32x4 o[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int s = s0 + u;
+      ls[u] = s < S ? gload<float>(p.ws_lse + s * plane + rh) : -INFINITY;
+      o[u] = s < S ? gload<f32x4>(src + s * step4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (s0 + u >= S) break;
+      const float m_new = fmaxf(M, ls[u]);
+      const float a = m_new == -INFINITY ? 1.f : __expf(M - m_new);  // rescale of the sum so far
+      const float b = ls[u] == -INFINITY ? 0.f : __expf(ls[u] - m_new);  // weight of split s
+      den = den * a + b;
+      num = num * a + b * o[u];
+      M = m_new;
+    }
   }
   const float inv = 1.f / den;
   const u32x2 v = {f32_to_bf16_bits(num[0] * inv) | (f32_to_bf16_bits(num[1] * inv) << 16),
