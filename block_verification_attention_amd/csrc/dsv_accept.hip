@@ -222,9 +222,17 @@ __global__ __launch_bounds__(kWave) void accept_finalize_kernel(
   if (keys) {
     int end = offsets[n_bs];
     end = end < 0 ? 0 : (end > m_bs ? m_bs : end);
-    // every slot's choice: grid-stride over all m_bs slots
-    for (int64_t s = (int64_t)i * kWave + lane; s < m_bs; s += (int64_t)n_bs * kWave)
-      slot_argmax[s] = s < end ? key_to_index(max_chunk_key(keys, s, n_chunks, 0, 1)) : -1;
+    // every slot's choice: 16 slots per wavefront pass, four lanes per slot (each reducing a
+    // quarter of the slot's chunk keys with its loads in flight together)
+    for (int64_t sb = (int64_t)i * 16; sb < m_bs; sb += (int64_t)n_bs * 16) {
+      const int64_t s = sb + (lane >> 2);
+      uint64_t kr = s < end ? max_chunk_key(keys, s, n_chunks, lane & 3, 4) : 0;
+      uint64_t o = shfl_xor_u64(kr, 1);
+      kr = o > kr ? o : kr;
+      o = shfl_xor_u64(kr, 2);
+      kr = o > kr ? o : kr;
+      if ((lane & 3) == 0 && s < m_bs) slot_argmax[s] = s < end ? key_to_index(kr) : -1;
+    }
 
     const int ki = k[i], off = offsets[i];
     const bool ok = ki >= 0 && ki <= W && off >= 0 && (int64_t)off + ki <= end;
