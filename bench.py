@@ -39,9 +39,9 @@ PROFILED_KERNEL = "attn_bf16_kernel<128, 8, false, 64, 2, false, 1>"
 # WRITE_SIZE runs (profiles/attn_verify_cfg3_hbm_traffic.md, calibrated there against the
 # streaming-read probe and a pool copy), valid for the kernel source with this SHA-256 only.
 COUNTED_SOURCE = ("block_verification_attention_amd/csrc/dsv_attn.hip",
-                  "9c73ed1d3eb711731debce0f8959cc09ef201dcd60204b6975f5048b922a350c")
-COUNTED_READ_BYTES = 270_569_711
-COUNTED_WRITE_BYTES = 9_470_116
+                  "535adeb083313671761bc7c26028eb7d5086475592c0611a23817fde9e82baea")
+COUNTED_READ_BYTES = 270_331_868
+COUNTED_WRITE_BYTES = 9_450_760
 
 
 def counted_traffic():

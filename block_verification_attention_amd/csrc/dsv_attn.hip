@@ -603,11 +603,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
 
   // Candidate block: K and V rows 0 .. k_i - 1 (from k_new, else from the pool) in the layout of
   // a 32-row tile of LDS stage 1, V rows k_i .. 31 zero (they meet zero probabilities in the
-  // 32-row P.V step).  Loaded in one batch per thread.
+  // 32-row P.V step).  Loaded in one batch per thread, ahead of the first tile's loads, so that
+  // staging them waits only for themselves (loads complete in issue order).
   constexpr int CPH = 2 * 16 * (D / 8);  // pieces of K and V rows 0..15
   constexpr int CPB = (CPH + NW * 64 - 1) / (NW * 64);
-  auto stage_candidates = [&]() __attribute__((always_inline)) {
-    Piece xc[CPB];
+  auto load_candidates = [&](Piece (&xc)[CPB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int b = 0; b < CPB; ++b) {
       const int e = b * NW * 64 + tid;
@@ -622,6 +622,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
         xc[b] = Piece{v[0], v[1], v[2], v[3]};
       }
     }
+  };
+  auto store_candidates = [&](const Piece (&xc)[CPB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int b = 0; b < CPB; ++b) {
       const int e = b * NW * 64 + tid;
@@ -643,21 +645,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
   // other stage, which every wave finished reading before the previous barrier, and reuses the
   // freed register set for tile t + 1 + RSETS.  One barrier per tile.
   Piece xa[QPW], xb[QPW];
-  if (n_tiles > 0) load_tile(r_lo, xa);
   if constexpr (!PF) {
     if (has_cand) {
-      stage_candidates();  // into stage 1, which the loop first writes after a barrier
-      if (n_tiles > 0) store_tile(xa, 0);
-      if (n_tiles > 1) load_tile(r_lo + (HV * TILE), RSETS == 2 ? xb : xa);
-      if (RSETS == 2 && n_tiles > 2) load_tile(r_lo + 2 * (HV * TILE), xa);
+      // The candidate block is staged (into stage 1, which the loop first writes after a
+      // barrier) and consumed while the first tiles are still in flight; tile 0 is stored after.
+      Piece xc[CPB];
+      load_candidates(xc);
+      if (n_tiles > 0) load_tile(r_lo, xa);
+      if (RSETS == 2 && n_tiles > 1) load_tile(r_lo + (HV * TILE), xb);
+      store_candidates(xc);
       __syncthreads();
       if (wave_live && half == 0)
         compute_tile(c, r_hi, std::integral_constant<int, 1>{}, std::integral_constant<bool, true>{},
                      std::integral_constant<int, 32>{});
+      if (n_tiles > 0) store_tile(xa, 0);
+      if (RSETS == 2) {
+        if (n_tiles > 2) load_tile(r_lo + 2 * (HV * TILE), xa);
+      } else {
+        if (n_tiles > 1) load_tile(r_lo + (HV * TILE), xa);
+      }
       __syncthreads();
     }
   }
   if (!has_cand) {
+    if (n_tiles > 0) load_tile(r_lo, xa);
     if constexpr (RSETS == 2) {
       if (n_tiles > 1) load_tile(r_lo + (HV * TILE), xb);
       if (n_tiles > 0) store_tile(xa, 0);
