@@ -13,11 +13,12 @@
 //     beats the list's last entry, which after the first few blocks is rare, so the common
 //     cost per value is one comparison (a lane first compares the maximum of its 32 values
 //     of the block).  Alongside, each lane keeps online statistics relative to its running
-//     maximum m: S = sum e^(z - m) and U = sum e^(z - m) (z - m).  The workgroup merges its
-//     four lists and statistics into one partial record per (row, chunk).
+//     maximum m, in log2 units (z2 = z log2 e, m2 = m log2 e): S = sum 2^(z2 - m2) and
+//     U = sum 2^(z2 - m2) (z2 - m2), so that each value costs one fma for its exponent.  The
+//     workgroup merges its four lists and statistics into one partial record per (row, chunk).
 //  2. feat_finalize_kernel -- one wavefront per row merges the chunk records and writes the
 //     18 features: top = l[0], gaps fp32(l[0] - l[r - 1]), log p(top) = -ln S (S relative to
-//     the top logit), entropy = ln S - U / S.
+//     the top logit), entropy = ln S - U ln 2 / S.
 #include "dsv_internal.h"
 
 namespace dsv {
@@ -32,11 +33,11 @@ constexpr float kLn2 = 0.69314718055994531f;
 
 struct FeatPart {
   float top[kTopK];  // the chunk's 16 largest values, descending (-inf where fewer)
-  float m, S, U;     // statistics relative to m (the chunk maximum); S = 0 if none is finite
+  float m, S, U;     // statistics relative to m (the chunk maximum, log2 units); S = 0 if none is finite
   int32_t bad;       // a NaN or +inf logit
 };
 
-// Online statistics: add the value set summarised by (m2, S2, U2) to (m, S, U).
+// Online statistics (log2 units): add the value set summarised by (m2, S2, U2) to (m, S, U).
 __device__ __forceinline__ void ent_merge(float &m, float &S, float &U, float m2, float S2, float U2) {
   if (S2 == 0.f) return;
   if (S == 0.f) {
@@ -47,7 +48,7 @@ __device__ __forceinline__ void ent_merge(float &m, float &S, float &U, float m2
   }
   const float mn = fmaxf(m, m2);
   const float d1 = m - mn, d2 = m2 - mn;  // <= 0
-  const float r1 = __builtin_amdgcn_exp2f(d1 * kLog2e), r2 = __builtin_amdgcn_exp2f(d2 * kLog2e);
+  const float r1 = __builtin_amdgcn_exp2f(d1), r2 = __builtin_amdgcn_exp2f(d2);
   U = r1 * (U + d1 * S) + r2 * (U2 + d2 * S2);
   S = r1 * S + r2 * S2;
   m = mn;
@@ -114,24 +115,30 @@ __global__ __launch_bounds__(kFtThreads) void feat_partial_kernel(
   float l = -INFINITY, tau = -INFINITY;  // the wavefront's list (lanes 0-15) and its threshold
   float floor = -INFINITY;
   bool first = true;
-  float m = -INFINITY, S = 0.f, U = 0.f;
+  float m = -INFINITY, m2 = -INFINITY, S = 0.f, U = 0.f;  // m2 = m log2 e
   bool bad = false;
-  // one value: statistics (a larger value rescales the running sums first)
+  // a larger maximum rescales the running sums first
+  auto raise = [&](float e) __attribute__((always_inline)) {
+    const float e2 = e * kLog2e;
+    const float d = m2 - e2;  // <= 0 (-inf while S = 0)
+    const float r = __builtin_amdgcn_exp2f(d);
+    U = S > 0.f ? r * (U + d * S) : 0.f;
+    S = S > 0.f ? r * S : 0.f;
+    m = e;
+    m2 = e2;
+  };
+  // one value: 2^(z2 - m2) with its exponent from one fma; a -inf logit adds nothing (its
+  // weight is 0 and its exponent, clamped for the product, finite)
+  auto add1 = [&](float e) __attribute__((always_inline)) {
+    const float d = __builtin_fmaf(e, kLog2e, -m2);
+    const float w = __builtin_amdgcn_exp2f(d);
+    S += w;
+    U = __builtin_fmaf(w, fmaxf(d, -128.f), U);
+  };
   auto stat1 = [&](float e) __attribute__((always_inline)) {
     bad |= !(e < INFINITY) && e != -INFINITY;
-    if (e > m) {
-      const float d = m - e;
-      const float r = __builtin_amdgcn_exp2f(d * kLog2e);
-      U = S > 0.f ? r * (U + d * S) : 0.f;
-      S = S > 0.f ? r * S : 0.f;
-      m = e;
-    }
-    if (e > -INFINITY) {
-      const float d = e - m;
-      const float w = __builtin_amdgcn_exp2f(d * kLog2e);
-      S += w;
-      U = fmaf(w, d, U);
-    }
+    if (e > m) raise(e);
+    if (e > -INFINITY) add1(e);
   };
   if (vec4) {
     constexpr int64_t kStep = 4 * kFtThreads;
@@ -152,23 +159,12 @@ __global__ __launch_bounds__(kFtThreads) void feat_partial_kernel(
           bad |= e != e;
           bm = fmaxf(bm, e);
         }
-      if (bm > m) {
-        const float d = m - bm;
-        const float r = __builtin_amdgcn_exp2f(d * kLog2e);
-        U = S > 0.f ? r * (U + d * S) : 0.f;
-        S = S > 0.f ? r * S : 0.f;
-        m = bm;
-      }
+      if (bm > m) raise(bm);
       if (m > -INFINITY) {
 #pragma unroll
         for (int u = 0; u < kFtLoads; ++u)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float d = f[u][q] - m;
-            const float w = __builtin_amdgcn_exp2f(d * kLog2e);
-            S += w;
-            U = w > 0.f ? fmaf(w, d, U) : U;
-          }
+          for (int q = 0; q < 4; ++q) add1(f[u][q]);
       }
       // list: only lanes whose block maximum beats the threshold look further
       if (first) {
@@ -211,6 +207,7 @@ __global__ __launch_bounds__(kFtThreads) void feat_partial_kernel(
     }
   }
   bad |= m == INFINITY;
+  m = m2;  // the records carry the maximum in log2 units
   // merge the lanes' statistics
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) {
@@ -287,7 +284,7 @@ __global__ __launch_bounds__(kWave) void feat_finalize_kernel(int64_t rows, int 
   if (lane == 0) f[0] = top;
   else if (lane < kTopK) f[lane] = top - l;
   else if (lane == kTopK) f[kTopK] = -lnS;
-  else if (lane == kTopK + 1) f[kTopK + 1] = lnS - U / S;
+  else if (lane == kTopK + 1) f[kTopK + 1] = lnS - U * kLn2 / S;
 }
 
 // Sweep chunking: about 2048 workgroups, chunks of whole 1024-element groups (four per lane).
