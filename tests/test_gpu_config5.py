@@ -1,0 +1,119 @@
+"""Parity at the full size of the mixed launch whose parts the bench times (its long-context
+verification set and its prefill wide tile): 60 verification requests with ragged prefixes in
+a 480-slot budget and contexts U[8192, 32768], and 4 fresh prefill requests of 4096 causal
+rows, in ONE dsv_verify_attn call; 32 query / 8 KV heads, head_dim 128, bf16.
+
+The K/V pool (2 x 8 x 1.27M x 128, ~5 GB) is drawn on the device from seeded generators,
+N(0,1) * 0.5 rounded to bf16 (the workload's distribution; a numpy draw of that size would
+take minutes).  The oracle receives copies of only the KV segments it needs and checks
+sampled outputs: every slot and head of three verification requests (the shortest and the
+longest context, and the one at the median) and 16 rows of every prefill request (the first,
+the last and 14 seeded ones).  The candidate K/V written into the pool are checked bit for
+bit at the packed cache references of all 60 requests."""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+import oracle  # noqa: E402
+import workloads as wl  # noqa: E402
+from gpu_util import DEV, TOL, bits_of, compare_attn, to_dev, to_f64  # noqa: E402
+import block_verification_attention_amd as dsv  # noqa: E402
+
+
+def _dev_normal(seed, shape, scale=0.5):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    return (torch.randn(shape, generator=g, device=DEV) * scale).to(torch.bfloat16)
+
+
+def test_config5_mixed_launch_sampled():
+    c = wl.config5(draw=False)
+    hq, hkv, d, W = c["hq"], c["hkv"], c["d"], c["W"]
+    n, m_bs, pool_rows = c["n_bs"], c["m_bs"], c["pool_rows"]
+    pf = c["prefill"]
+    pf_rows = int(pf["q_len"].sum())
+    k_pool = _dev_normal(5101, (hkv, pool_rows, d))
+    v_pool = _dev_normal(5102, (hkv, pool_rows, d))
+    q = _dev_normal(5103, (m_bs, hq, d))
+    k_new = _dev_normal(5104, (m_bs, hkv, d))
+    v_new = _dev_normal(5105, (m_bs, hkv, d))
+    pf_q = _dev_normal(5109, (pf_rows, hq, d))
+
+    ref_pack = oracle.pack(c["k"], c["ctx_len"], c["kv_base"], c["block_tokens"], W, m_bs)
+    offs = ref_pack["offsets"]
+    live = np.flatnonzero(c["k"] > 0)
+    order = live[np.argsort(c["ctx_len"][live], kind="stable")]
+    sample = [int(order[0]), int(order[len(order) // 2]), int(order[-1])]
+
+    # the oracle's copies, taken before the call (it writes the candidates' K/V into the pool):
+    # each sampled request's committed context, then W spare rows
+    kb_m, kp_m, vp_m, rows = [], [], [], 0
+    for i in sample:
+        lo, cx = int(c["kv_base"][i]), int(c["ctx_len"][i])
+        kb_m.append(rows)
+        pad = torch.zeros((hkv, W, d), dtype=torch.bfloat16, device=DEV)
+        kp_m.append(torch.cat([k_pool[:, lo:lo + cx], pad], dim=1))
+        vp_m.append(torch.cat([v_pool[:, lo:lo + cx], pad], dim=1))
+        rows += cx + W
+    kp_m, vp_m = bits_of(torch.cat(kp_m, dim=1)), bits_of(torch.cat(vp_m, dim=1))
+    pf_lo = int(pf["kv_base"][0])
+    kp_pf = bits_of(k_pool[:, pf_lo:pf_lo + pf_rows])
+    vp_pf = bits_of(v_pool[:, pf_lo:pf_lo + pf_rows])
+    assert np.array_equal(pf["kv_base"] - pf_lo, np.asarray(pf["q_start"], np.int64))
+
+    st = dsv.new_status(DEV)
+    kd, cd, bd = to_dev(c["k"]), to_dev(c["ctx_len"]), to_dev(c["kv_base"])
+    packed = dsv.pack_slots(kd, cd, bd, to_dev(c["block_tokens"]), m_bs, st)
+    pf_out = torch.full_like(pf_q, float("nan"))
+    pf_lse = torch.full((pf_rows, hq), float("nan"), device=DEV)
+    prefill = dsv.Prefill(q_start=to_dev(pf["q_start"]), q_len=to_dev(pf["q_len"]),
+                          ctx_len=to_dev(pf["ctx_len"]), kv_base=to_dev(pf["kv_base"]), q=pf_q,
+                          out=pf_out, max_len=pf["max_len"], lse=pf_lse)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((m_bs, hq), float("nan"), device=DEV)
+    dsv.verify_attn(q, k_pool, v_pool, packed["offsets"], kd, cd, bd, W=W,
+                    max_ctx=int(c["ctx_len"].max()), status=st, out=out, lse=lse, k_new=k_new,
+                    v_new=v_new, slot_cache_loc=packed["slot_cache_loc"], prefill=prefill)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(packed["offsets"].cpu().numpy(), offs)
+
+    # candidate K/V at the packed cache references, all requests, bit for bit
+    loc = torch.as_tensor(ref_pack["slot_cache_loc"][:int(offs[-1])], device=DEV)
+    assert torch.equal(k_pool[:, loc].transpose(0, 1).view(torch.int16), k_new[:int(offs[-1])].view(torch.int16))
+    assert torch.equal(v_pool[:, loc].transpose(0, 1).view(torch.int16), v_new[:int(offs[-1])].view(torch.int16))
+
+    # verification rows of the sampled requests
+    k_m = np.array([c["k"][i] for i in sample], np.int32)
+    off_m = np.concatenate([[0], np.cumsum(k_m)]).astype(np.int32)
+    sl = [slice(int(offs[i]), int(offs[i]) + int(c["k"][i])) for i in sample]
+    pick = lambda t: torch.cat([t[s] for s in sl])  # noqa: E731
+    ref_o, ref_l = oracle.verify_attn(bits_of(pick(q)), kp_m, vp_m, off_m, k_m,
+                                      np.array([c["ctx_len"][i] for i in sample], np.int32),
+                                      np.array(kb_m, np.int64), k_new=bits_of(pick(k_new)),
+                                      v_new=bits_of(pick(v_new)))
+    mc = dict(n_bs=len(sample), k=k_m, hq=hq, dtype="bf16", m_bs=int(off_m[-1]))
+    compare_attn(mc, off_m, pick(out), pick(lse), ref_o, ref_l, tag="config 5 verification")
+
+    # prefill rows: first, last and 14 seeded per request
+    g = np.random.default_rng(5110)
+    sel_req, sel_j = [], []
+    for r in range(pf["n_pf"]):
+        ql = int(pf["q_len"][r])
+        js = sorted(set([0, ql - 1] + g.choice(np.arange(1, ql - 1), 14, replace=False).tolist()))
+        sel_req += [r] * len(js)
+        sel_j += js
+    ref_po, ref_pl = oracle.prefill_attn(bits_of(pf_q), kp_pf, vp_pf, pf["q_start"], pf["q_len"],
+                                         pf["ctx_len"], np.asarray(pf["q_start"], np.int64),
+                                         sel_req, sel_j)
+    idx = torch.as_tensor([int(pf["q_start"][r]) + j for r, j in zip(sel_req, sel_j)], device=DEV)
+    go, gl = to_f64(pf_out[idx]), to_f64(pf_lse[idx])
+    tol = TOL["bf16"]
+    assert np.all(np.isfinite(go))
+    assert np.abs(go - ref_po).max() <= tol["max_abs"], np.abs(go - ref_po).max()
+    for h in range(hq):
+        rel = np.linalg.norm(go[:, h] - ref_po[:, h]) / np.linalg.norm(ref_po[:, h])
+        assert rel <= tol["rel_l2"], (h, rel)
+    assert np.abs(gl - ref_pl).max() <= tol["lse"], np.abs(gl - ref_pl).max()

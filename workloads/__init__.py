@@ -266,23 +266,25 @@ def config4(with_draft_logits: bool = True) -> dict:
                      qkv_scale=0.5, draft_vocab=248320 if with_draft_logits else None)
 
 
-def config5() -> dict:
+def config5(draw: bool = True) -> dict:
     """Mixed launch, bf16: 4 prefill requests x 4096 causal rows (fresh, context 0) plus 60
     verification requests with ragged prefixes in a 480-slot budget and contexts
     U[8192, 32768]; 32/8 heads, head_dim 128.  The prefill rows' K/V are already in the pool,
-    in segments after the verification segments."""
+    in segments after the verification segments.  draw=False gives the layout only (lengths,
+    segments, tokens), without the ~5 GB of pool, query and candidate tensors."""
     g = rng(5, 0)
     k = lengths_geometric_rescaled(g, 60, 480)
     ctx = g.integers(8192, 32769, size=60).astype(np.int32)
     return make_mixed_case(5, hq=32, hkv=8, d=128, k=k, ctx_len=ctx, m_bs=480,
-                           pf_q_len=[4096] * 4, pf_ctx=[0] * 4, qkv_scale=0.5)
+                           pf_q_len=[4096] * 4, pf_ctx=[0] * 4, qkv_scale=0.5, draw=draw)
 
 
 def make_mixed_case(seed_config: int, *, hq, hkv, d, k, ctx_len, m_bs, pf_q_len, pf_ctx,
-                    qkv_scale=0.5, dtype="bf16") -> dict:
+                    qkv_scale=0.5, dtype="bf16", draw: bool = True) -> dict:
     """Verification batch plus prefill requests sharing one pool.  Prefill request r has
     pf_q_len[r] query rows at positions pf_ctx[r] .. pf_ctx[r] + len - 1; its segment holds
-    pf_ctx[r] + pf_q_len[r] rows, all already in the pool."""
+    pf_ctx[r] + pf_q_len[r] rows, all already in the pool.  draw=False leaves the pool, query
+    and candidate tensors out (None)."""
     k = np.asarray(k, np.int32)
     ctx_len = np.asarray(ctx_len, np.int32)
     pf_q_len = np.asarray(pf_q_len, np.int32)
@@ -294,11 +296,9 @@ def make_mixed_case(seed_config: int, *, hq, hkv, d, k, ctx_len, m_bs, pf_q_len,
     n = len(k)
     c = dict(name=f"cfg{seed_config}", dtype=dtype, W=W_BLOCK, hq=hq, hkv=hkv, d=d, n_bs=n,
              m_bs=m_bs, k=k, ctx_len=ctx_len, kv_base=kv_base, pool_rows=pool_rows)
-    c["k_pool"] = normal(rng(seed_config, 1), (hkv, pool_rows, d), qkv_scale, dtype)
-    c["v_pool"] = normal(rng(seed_config, 2), (hkv, pool_rows, d), qkv_scale, dtype)
-    c["q"] = normal(rng(seed_config, 3), (m_bs, hq, d), qkv_scale, dtype)
-    c["k_new"] = normal(rng(seed_config, 4), (m_bs, hkv, d), qkv_scale, dtype)
-    c["v_new"] = normal(rng(seed_config, 5), (m_bs, hkv, d), qkv_scale, dtype)
+    for key, t, shape in (("k_pool", 1, (hkv, pool_rows, d)), ("v_pool", 2, (hkv, pool_rows, d)),
+                          ("q", 3, (m_bs, hq, d)), ("k_new", 4, (m_bs, hkv, d)), ("v_new", 5, (m_bs, hkv, d))):
+        c[key] = normal(rng(seed_config, t), shape, qkv_scale, dtype) if draw else None
     c["block_tokens"] = rng(seed_config, 6).integers(0, 32000, size=(n, W_BLOCK)).astype(np.int32)
     c["vocab"] = None
     c["logits"] = None
@@ -308,7 +308,7 @@ def make_mixed_case(seed_config: int, *, hq, hkv, d, k, ctx_len, m_bs, pf_q_len,
         q_start[1:] = np.cumsum(pf_q_len)[:-1]
     c["prefill"] = dict(
         n_pf=len(pf_q_len), q_start=q_start, q_len=pf_q_len, ctx_len=pf_ctx, kv_base=pf_base,
-        q=normal(rng(seed_config, 9), (int(pf_q_len.sum()), hq, d), qkv_scale, dtype),
+        q=normal(rng(seed_config, 9), (int(pf_q_len.sum()), hq, d), qkv_scale, dtype) if draw else None,
         max_len=int(pf_q_len.max()) if len(pf_q_len) else 0,
     )
     return c
