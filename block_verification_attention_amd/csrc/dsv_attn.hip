@@ -240,6 +240,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
 
   // ---- work unit ----
   int g, h, c, r_lo, r_hi, row0, nrows, split = 0, n_splits_i = 1, off = 0, hg = 0;
+  // verification: query row of this lane's column and whether its head slot exists
+  int col_row = 0;
+  bool col_ok = true, wave_has_heads = true;
   int64_t kb, q_row0;
   const uint16_t *qsrc;
   const uint16_t *knew = nullptr, *vnew = nullptr;
@@ -293,6 +296,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     nrows = ki;
     q_row0 = off;
     qsrc = static_cast<const uint16_t *>(p.q);
+    // Head packing: the 16 columns of a wave's tile are independent (query head, row) pairs
+    // that share the K and V operands, so a request with k_i rows fills a tile with
+    // 16 / R heads of R rows (R = k_i rounded up to a power of two).  The workgroup's waves
+    // then take 16 / R heads each and those left without a head skip the tile arithmetic.
+    int R = 1;
+    while (R < ki) R <<= 1;
+    const int slot = wh * (16 / R) + lq / R;  // head slot of this lane's column
+    col_ok = slot < p.GW;
+    col_row = lq % R;
+    wave_has_heads = wh * (16 / R) < p.GW;
+    h = h0 + (col_ok ? slot : 0);
     if (p.k_new) {
       knew = static_cast<const uint16_t *>(p.k_new);
       vnew = static_cast<const uint16_t *>(p.v_new);
@@ -334,10 +348,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
   (void)n_splits_i;
 
   // ---- query fragment (B operand of S^T = K Q^T): row lq, columns 32ks + 8lg .. +7 ----
-  const int my_row = PF ? row0 + w * 16 + lq : lq;  // query row index within the request
+  const int my_row = PF ? row0 + w * 16 + lq : col_row;  // query row index within the request
   bf16x8 qf[KS];
   {
-    const bool ok = my_row < nrows;
+    const bool ok = my_row < nrows && col_ok;
     const uint16_t *qp = qsrc + ((q_row0 + (ok ? my_row : 0)) * p.hq + h) * (int64_t)D + 8 * lg;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -502,7 +516,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
 
   const int n_tiles = (t_hi - r_lo + HV * TILE - 1) / (HV * TILE);  // stages of HV tiles
   const int wave_row_lo = PF ? row0 + w * 16 : 0;
-  const bool wave_live = wave_row_lo < nrows;
+  const bool wave_live = wave_row_lo < nrows && wave_has_heads;
   const float sl2 = p.scale_log2;
 
   // One tile of ROWS (TILE, or 32 for the candidate block) KV rows at positions base.. from
@@ -762,7 +776,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
   // full row sum across the four lane groups holding the row
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  if (my_row >= nrows) return;
+  if (my_row >= nrows || !col_ok) return;
   const bool empty = !(l_run > 0.f);
   const float inv_l = empty ? 0.f : 1.f / l_run;
   const float lse_v = empty ? -INFINITY : (m_ref + __builtin_amdgcn_logf(l_run)) * 0.69314718055994530942f;
