@@ -39,9 +39,9 @@ PROFILED_KERNEL = "attn_bf16_kernel<128, 8, false, 64, 2, false, 1>"
 # WRITE_SIZE runs (profiles/attn_verify_cfg3_hbm_traffic.md, calibrated there against the
 # streaming-read probe and a pool copy), valid for the kernel source with this SHA-256 only.
 COUNTED_SOURCE = ("block_verification_attention_amd/csrc/dsv_attn.hip",
-                  "535adeb083313671761bc7c26028eb7d5086475592c0611a23817fde9e82baea")
-COUNTED_READ_BYTES = 270_331_868
-COUNTED_WRITE_BYTES = 9_450_760
+                  "34f04651d90687b706f1c303fb513de3530272dd2f05ec05f4372381f2c0a857")
+COUNTED_READ_BYTES = 270_331_741
+COUNTED_WRITE_BYTES = 9_444_696
 
 
 def counted_traffic():
