@@ -272,7 +272,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     if (i == 0 && split == 0) {
       int end = p.offsets[p.n_bs];
       end = end < 0 ? 0 : (end > p.m_bs ? p.m_bs : end);
-      zero_rows_bf16<D>(static_cast<uint16_t *>(p.out), p.lse, p.hq, end, p.m_bs, h0, p.GW,
+      zero_rows_bf16<D>(static_cast<uint16_t *>(p.out), p.lse, p.hq, end, p.m_bs, h0,
+                        min(p.GW, p.G - hg * p.GW),
                         tid, NW * 64);
     }
     int ki;
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
         if (tid == 0 && g == 0 && hg == 0) status_or(p.status, bad);
         if (ki >= 0 && ki <= p.W && off >= 0 && (int64_t)off + ki <= p.m_bs)
           zero_rows_bf16<D>(static_cast<uint16_t *>(p.out), p.lse, p.hq, off, off + ki, h0,
-                            p.GW, tid, NW * 64);
+                            min(p.GW, p.G - hg * p.GW), tid, NW * 64);
       }
       return;
     }
@@ -303,9 +304,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     int R = 1;
     while (R < ki) R <<= 1;
     const int slot = wh * (16 / R) + lq / R;  // head slot of this lane's column
-    col_ok = slot < p.GW;
+    const int heads_here = min(p.GW, p.G - hg * p.GW);  // the last group may be partial
+    col_ok = slot < heads_here;
     col_row = lq % R;
-    wave_has_heads = wh * (16 / R) < p.GW;
+    wave_has_heads = wh * (16 / R) < heads_here;
     h = h0 + (col_ok ? slot : 0);
     if (p.k_new) {
       knew = static_cast<const uint16_t *>(p.k_new);
@@ -1045,22 +1047,21 @@ constexpr int kWideHeadsPerWg = DSV_WIDE_HEADS_PER_WG;
 // Query heads per verification workgroup.  For head_dim 256 a head's output accumulators
 // (64 registers per lane) plus its query fragment do not leave room for the rest of a wave's
 // state at two or three waves per SIMD, so each head gets two waves that split the output
-// columns (verify_waves_per_head), and a KV head's query heads are spread over G / GW
-// workgroups of 2 GW waves, which each read the KV head's rows: GW = the largest divisor of
-// G not above kWideHeadsPerWg.  Head_dim 128 keeps groups of up to 8 heads whole.
+// columns (verify_waves_per_head), and a KV head's query heads are spread over
+// HG = ceil(G / GW) workgroups of 2 GW waves, which each read the KV head's rows, with at
+// most kWideHeadsPerWg heads each.  At head_dim 128 more than 8 one-head waves per
+// workgroup would run at 3-4 waves per SIMD and spill, so larger groups are split the same
+// way into workgroups of at most 8 heads.  The groups are as even as possible (the last one
+// may hold fewer heads: its spare waves only move tile loads).
 static int verify_heads_per_wg(int D, int G) {
-  if (D >= 256) {
-    for (int gw = kWideHeadsPerWg; gw > 1; --gw)
-      if (G % gw == 0) return gw;
-    return 1;
-  }
-  // head_dim 128: more than 8 one-head waves per workgroup run at 3-4 waves per SIMD and
-  // spill; split the group into workgroups of at most 8 heads when G has such a divisor
-  if (D >= 128 && G > 8) {
-    for (int gw = 8; gw > 1; --gw)
-      if (G % gw == 0) return gw;
-  }
-  return G;
+  const int cap = D >= 256 ? kWideHeadsPerWg : (D >= 128 ? 8 : G);
+  if (G <= cap) return G;
+  const int groups = (G + cap - 1) / cap;
+  return (G + groups - 1) / groups;
+}
+static int verify_head_groups(int D, int G) {
+  const int gw = verify_heads_per_wg(D, G);
+  return (G + gw - 1) / gw;
 }
 
 // Waves per query head in the verification kernel (output columns split between them).
@@ -1082,7 +1083,7 @@ static Plan make_plan(const dsv_attn_args *a) {
   if (chunk <= 0) {
     const int G = a->hkv > 0 ? a->hq / a->hkv : 1;
     const int GW = verify_heads_per_wg(a->d, G);
-    const int64_t units = (int64_t)a->n_bs * a->hkv * (G / GW);
+    const int64_t units = (int64_t)a->n_bs * a->hkv * verify_head_groups(a->d, G);
     // wave groups in flight: two per SIMD (512 groups of G waves, or 256 two-half ones); the
     // wide-head workgroups (2 GW waves, one per CU at a time) aim at four rounds, whose
     // shorter splits balance requests of different lengths (32 requests at 4k-8k with 12
@@ -1253,7 +1254,7 @@ extern "C" dsv_status dsv_verify_attn(const dsv_attn_args *a, hipStream_t stream
   p.hkv = a->hkv;
   p.G = G;
   p.GW = verify_heads_per_wg(a->d, G);
-  p.HG = G / p.GW;
+  p.HG = verify_head_groups(a->d, G);
   p.scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.0f / sqrtf((float)a->d);
   p.scale_log2 = p.scale * 1.4426950408889634f;
   p.n_bs = a->n_bs;

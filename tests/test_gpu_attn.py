@@ -31,7 +31,11 @@ def test_config1_fp32():
 
 @pytest.mark.parametrize("d_head,hq,hkv", [(64, 4, 1), (128, 8, 2), (128, 32, 8), (256, 24, 2),
                                             (128, 12, 4), (256, 4, 4), (128, 16, 1), (128, 24, 2),
-                                            (256, 8, 1), (256, 6, 2), (64, 16, 2), (128, 13, 1)])
+                                            (256, 8, 1), (256, 6, 2), (64, 16, 2), (128, 13, 1),
+                                            # groups split unevenly over workgroups (the last
+                                            # one holds fewer heads)
+                                            (128, 9, 1), (128, 11, 1), (256, 5, 1), (256, 7, 1),
+                                            (256, 10, 1), (256, 13, 1)])
 @pytest.mark.parametrize("kv_chunk", [0, 64, 256])
 def test_bf16_ragged(d_head, hq, hkv, kv_chunk):
     if (d_head, hq, hkv) == (256, 4, 4):
