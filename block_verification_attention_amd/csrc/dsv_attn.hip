@@ -1055,9 +1055,13 @@ constexpr int kWideHeadsPerWg = DSV_WIDE_HEADS_PER_WG;
 // may hold fewer heads: its spare waves only move tile loads).
 static int verify_heads_per_wg(int D, int G) {
   const int cap = D >= 256 ? kWideHeadsPerWg : (D >= 128 ? 8 : G);
-  if (G <= cap) return G;
   const int groups = (G + cap - 1) / cap;
-  return (G + groups - 1) / groups;
+  int gw = (G + groups - 1) / groups;
+  // head_dim 128: workgroups of 2, 3 or 6 one-head waves spill (the tile's wave loads do not
+  // split evenly over them); such groups run padded to 4 or 8 heads
+  if (D == 128 && (gw == 2 || gw == 3)) gw = 4;
+  if (D == 128 && gw == 6) gw = 8;
+  return gw;
 }
 static int verify_head_groups(int D, int G) {
   const int gw = verify_heads_per_wg(D, G);
@@ -1166,8 +1170,20 @@ static int launch_verify_g(const AttnParams &p, int grid, hipStream_t s, hipEven
       case 4: return launch_attn<D, 8, false, 1, 2>(p, grid, s, e0, e1);
       default: return -1;
     }
+  } else if constexpr (D == 128) {
+    // groups padded to 1 or 4 heads (two KV halves) or 5, 7, 8 heads (one half): the shapes
+    // that fit two waves per SIMD without spilling
+    switch (p.GW) {
+      case 1: return launch_attn<D, 2, false, 2>(p, grid, s, e0, e1);
+      case 4: return launch_attn<D, 8, false, 2>(p, grid, s, e0, e1);
+      case 5: return launch_attn<D, 5, false>(p, grid, s, e0, e1);
+      case 7: return launch_attn<D, 7, false>(p, grid, s, e0, e1);
+      case 8: return launch_attn<D, 8, false>(p, grid, s, e0, e1);
+      default: return -1;
+    }
   } else {
-    // groups of up to 4 heads: two KV halves (verify_halves)
+    // head_dim 64: every group of up to 16 heads in one workgroup; up to 4 heads in two KV
+    // halves (verify_halves)
     switch (p.GW) {
       case 1: return launch_attn<D, 2, false, 2>(p, grid, s, e0, e1);
       case 2: return launch_attn<D, 4, false, 2>(p, grid, s, e0, e1);

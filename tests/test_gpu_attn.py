@@ -33,9 +33,9 @@ def test_config1_fp32():
                                             (128, 12, 4), (256, 4, 4), (128, 16, 1), (128, 24, 2),
                                             (256, 8, 1), (256, 6, 2), (64, 16, 2), (128, 13, 1),
                                             # groups split unevenly over workgroups (the last
-                                            # one holds fewer heads)
+                                            # one holds fewer heads) or padded to a wider one
                                             (128, 9, 1), (128, 11, 1), (256, 5, 1), (256, 7, 1),
-                                            (256, 10, 1), (256, 13, 1)])
+                                            (256, 10, 1), (256, 13, 1), (128, 2, 1), (128, 6, 1)])
 @pytest.mark.parametrize("kv_chunk", [0, 64, 256])
 def test_bf16_ragged(d_head, hq, hkv, kv_chunk):
     if (d_head, hq, hkv) == (256, 4, 4):
