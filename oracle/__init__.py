@@ -23,6 +23,8 @@ full definitions):
   DFlash7-ACT margin of DFlash-Mini-Lab.
 * ``draft_features``: the 18 per-position confidence values of DScale Sec. III-C
   (Acceptance predictor).
+* ``philox_raw`` / ``philox_uniforms``: the counter-based generator for the sampling
+  verifier's uniforms, Philox4x64-10 as published by Salmon et al. (SC 2011).
 """
 from __future__ import annotations
 
@@ -89,6 +91,9 @@ def _load():
         lib.oracle_accept_sample.argtypes = [i32, i32, i32, i64, P, dbl] + [P] * 12
         lib.oracle_threads.argtypes = []
         lib.oracle_allocate.argtypes = [i32, i32, i32, i32, P, P, P]
+        u64 = ctypes.c_uint64
+        lib.oracle_philox_raw.argtypes = [u64, u64, u64, u64, i64, P]
+        lib.oracle_philox_uniforms.argtypes = [u64, u64, u64, u64, i64, P]
         _lib = lib
     return _lib
 
@@ -441,3 +446,31 @@ def draft_features(draft_logits):
     feat = np.zeros((rows, 18), np.float32)
     _check(lib.oracle_draft_features(rows, vocab, _p(x), _p(feat)))
     return feat.reshape(lead + (18,))
+
+
+def _split128(v):
+    v = int(v)
+    if v < 0 or v >= 1 << 128:
+        raise OracleError("key and counter are 128-bit unsigned integers")
+    return v & ((1 << 64) - 1), v >> 64
+
+
+def philox_raw(key, counter, n):
+    """n 64-bit words of Philox4x64-10 (Salmon et al., SC 2011) under a 128-bit key: word i is
+    word i % 4 of the block at the 128-bit counter `counter + i // 4`."""
+    lib = _load()
+    k0, k1 = _split128(key)
+    c0, c1 = _split128(counter)
+    out = np.zeros(int(n), np.uint64)
+    _check(lib.oracle_philox_raw(k0, k1, c0, c1, int(n), _p(out)))
+    return out
+
+
+def philox_uniforms(key, counter, n):
+    """float32 uniforms in [0, 1): the top 24 bits of each word of philox_raw, times 2^-24."""
+    lib = _load()
+    k0, k1 = _split128(key)
+    c0, c1 = _split128(counter)
+    out = np.zeros(int(n), np.float32)
+    _check(lib.oracle_philox_uniforms(k0, k1, c0, c1, int(n), _p(out)))
+    return out

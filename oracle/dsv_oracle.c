@@ -739,6 +739,64 @@ int oracle_draft_features(int64_t rows, int64_t vocab, const float *logits, floa
   return err;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Counter-based uniforms for the sampling verifier's draws.                  */
+/*                                                                            */
+/* Philox4x64-10 as defined by Salmon, Moraes, Dror and Shaw, "Parallel       */
+/* random numbers: as easy as 1, 2, 3" (SC 2011): a 256-bit counter block     */
+/* (x0, x1, x2, x3) and a 128-bit key (k0, k1) go through ten rounds; a round */
+/* multiplies x0 and x2 by the two round multipliers into 128-bit products    */
+/* and produces (hi(M1 x2) ^ x1 ^ k0, lo(M1 x2), hi(M0 x0) ^ x3 ^ k1,         */
+/* lo(M0 x0)); between rounds the key is bumped by the two Weyl constants.    */
+/* Output i of a stream is word i % 4 of the block at counter c + i / 4       */
+/* (c a 128-bit base held in the two low counter words, carried); its         */
+/* uniform is the top 24 bits times 2^-24, exactly representable in fp32 and  */
+/* in [0, 1).                                                                 */
+/* ------------------------------------------------------------------------ */
+static void philox4x64_10(uint64_t x[4], uint64_t k0, uint64_t k1) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+  for (int r = 0; r < 10; ++r) {
+    const unsigned __int128 p0 = (unsigned __int128)M0 * x[0];
+    const unsigned __int128 p1 = (unsigned __int128)M1 * x[2];
+    const uint64_t y0 = (uint64_t)(p1 >> 64) ^ x[1] ^ k0;
+    const uint64_t y1 = (uint64_t)p1;
+    const uint64_t y2 = (uint64_t)(p0 >> 64) ^ x[3] ^ k1;
+    const uint64_t y3 = (uint64_t)p0;
+    x[0] = y0;
+    x[1] = y1;
+    x[2] = y2;
+    x[3] = y3;
+    k0 += W0;
+    k1 += W1;
+  }
+}
+
+/* Raw 64-bit words: out[i] = word i % 4 of the block at counter (ctr_lo, ctr_hi) + i / 4. */
+int oracle_philox_raw(uint64_t key0, uint64_t key1, uint64_t ctr_lo, uint64_t ctr_hi, int64_t n,
+                      uint64_t *out) {
+  if (n < 0) return OR_ERR_ARG;
+  for (int64_t b = 0; 4 * b < n; ++b) {
+    const uint64_t lo = ctr_lo + (uint64_t)b;
+    uint64_t x[4] = {lo, ctr_hi + (lo < ctr_lo ? 1u : 0u), 0, 0};
+    philox4x64_10(x, key0, key1);
+    for (int j = 0; j < 4 && 4 * b + j < n; ++j) out[4 * b + j] = x[j];
+  }
+  return OR_OK;
+}
+
+/* Uniforms: out[i] = (word i >> 40) * 2^-24. */
+int oracle_philox_uniforms(uint64_t key0, uint64_t key1, uint64_t ctr_lo, uint64_t ctr_hi,
+                           int64_t n, float *out) {
+  if (n < 0) return OR_ERR_ARG;
+  uint64_t *raw = malloc((size_t)(n > 0 ? n : 1) * sizeof(uint64_t));
+  if (!raw) return OR_ERR_ARG;
+  oracle_philox_raw(key0, key1, ctr_lo, ctr_hi, n, raw);
+  for (int64_t i = 0; i < n; ++i) out[i] = (float)ldexp((double)(raw[i] >> 40), -24);
+  free(raw);
+  return OR_OK;
+}
+
 #ifdef _OPENMP
 #include <omp.h>
 #endif
