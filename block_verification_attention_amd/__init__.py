@@ -17,6 +17,7 @@ from .api import (
     allocate_pack,
     draft_features,
     draft_features_workspace_bytes,
+    philox_uniforms,
     accept_workspace_bytes,
     attn_args,
     new_status,
@@ -30,7 +31,7 @@ __all__ = [
     "DsvError", "MAX_W", "STATUS_BAD_REQUEST", "STATUS_BUDGET", "STATUS_NAN", "STATUS_POOL",
     "STATUS_PREFILL", "Prefill", "accept", "accept_sample", "accept_sample_workspace_bytes",
     "accept_workspace_bytes", "allocate_pack", "attn_args",
-    "draft_features", "draft_features_workspace_bytes", "new_status",
+    "draft_features", "draft_features_workspace_bytes", "philox_uniforms", "new_status",
     "pack_slots", "verify_attn", "verify_attn_call", "verify_attn_workspace_bytes",
 ]
 

@@ -90,6 +90,9 @@ def load():
     lib.dsv_draft_features_workspace_bytes.restype = ctypes.c_size_t
     lib.dsv_draft_features.argtypes = [ctypes.c_int64, i32, P, P, P, ctypes.c_size_t, P, P]
     lib.dsv_draft_features.restype = ctypes.c_int
+    u64 = ctypes.c_uint64
+    lib.dsv_philox_uniforms.argtypes = [u64, u64, u64, u64, ctypes.c_int64, P, P]
+    lib.dsv_philox_uniforms.restype = ctypes.c_int
     lib.dsv_probe_stream_read.argtypes = [P, ctypes.c_size_t, P, P]
     lib.dsv_probe_stream_read.restype = ctypes.c_int
     if lib.dsv_attn_args_size() != ctypes.sizeof(AttnArgs):

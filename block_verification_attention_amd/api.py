@@ -2,7 +2,7 @@
 
 Every step runs in the HIP kernels of libdsv.so; PyTorch provides device memory and the
 stream.  Names follow the C ABI (include/dsv.h): pack_slots, allocate_pack, verify_attn,
-accept, accept_sample, draft_features.
+accept, accept_sample, draft_features, philox_uniforms.
 """
 from __future__ import annotations
 
@@ -321,4 +321,27 @@ def draft_features(draft_logits, status, out=None, workspace=None, stream=None):
     check(lib.dsv_draft_features(rows, vocab, _ptr(draft_logits), _ptr(out), _ptr(workspace),
                                  workspace.numel() if workspace is not None else 0, _ptr(status),
                                  _stream(stream)), "dsv_draft_features")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# dsv_philox_uniforms
+# ---------------------------------------------------------------------------
+def philox_uniforms(key: int, counter: int, n: int, device=None, out=None, stream=None):
+    """n float32 uniforms in [0, 1) from Philox4x64-10 under the 128-bit key, starting at the
+    128-bit counter (ceil(n / 4) counter values are consumed)."""
+    lib = _lib.load()
+    key, counter = int(key), int(counter)
+    if not (0 <= key < 1 << 128 and 0 <= counter < 1 << 128):
+        raise DsvError(1, "dsv_philox_uniforms")
+    if out is None:
+        if device is None:
+            raise ValueError("philox_uniforms: give the device or an output tensor")
+        out = torch.empty(int(n), dtype=torch.float32, device=device)
+    if out.device.type != "cuda" or out.numel() < int(n):
+        raise ValueError("philox_uniforms: out must be a GPU tensor of at least n floats")
+    _need(out, torch.float32, "out", out.device)
+    m = (1 << 64) - 1
+    check(lib.dsv_philox_uniforms(key & m, key >> 64, counter & m, counter >> 64, int(n), _ptr(out),
+                                  _stream(stream)), "dsv_philox_uniforms")
     return out

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdsv.so")
-SOURCES = ["dsv_pack.hip", "dsv_attn.hip", "dsv_accept.hip", "dsv_sample.hip", "dsv_features.hip", "dsv_status.hip", "dsv_probe.hip"]
+SOURCES = ["dsv_pack.hip", "dsv_attn.hip", "dsv_accept.hip", "dsv_sample.hip", "dsv_features.hip", "dsv_rng.hip", "dsv_status.hip", "dsv_probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

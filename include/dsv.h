@@ -368,6 +368,27 @@ dsv_status dsv_draft_features(int64_t rows, int32_t vocab, const float *draft_lo
                               int32_t *status, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* dsv_philox_uniforms -- counter-based uniforms for the sampling verifier   */
+/*                                                                            */
+/* DScale Sec. III-D (Prefix verifier, sampling mode: the accept test and    */
+/* the successor draw each take a uniform), generated on the device with     */
+/* Philox4x64-10 as defined by Salmon et al., "Parallel random numbers: as   */
+/* easy as 1, 2, 3" (SC 2011), so that a serving loop (or a captured graph)  */
+/* can refill u_accept / u_draw of dsv_accept_sample without the host.       */
+/*                                                                            */
+/* out[i] (f32, device) = (w_i >> 40) * 2^-24, w_i = 64-bit word i % 4 of    */
+/*   the Philox4x64-10 block at the 128-bit counter                           */
+/*   (counter_hi:counter_lo) + i / 4 (carried into counter_hi; the two high  */
+/*   counter words are 0) under the key (key1:key0).  Values are multiples   */
+/*   of 2^-24 in [0, 1).  A stream of n values consumes ceil(n / 4) counter  */
+/*   values, so consecutive calls can advance the counter by that much.      */
+/* Errors  host: DSV_ERR_INVALID_ARG (n < 0, out null with n > 0, more than  */
+/*   2^31 workgroups), DSV_ERR_HIP.  n = 0 enqueues nothing.                  */
+/* ------------------------------------------------------------------------ */
+dsv_status dsv_philox_uniforms(uint64_t key0, uint64_t key1, uint64_t counter_lo,
+                               uint64_t counter_hi, int64_t n, float *out, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* dsv_probe_stream_read -- measurement helper (not part of the method)      */
 /*                                                                            */
 /* Reads `bytes` (rounded down to 16) of device memory at `buf` (16-byte     */

@@ -61,6 +61,10 @@ def test_host_validation_without_gpu():
                           ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16),
                           ctypes.c_void_p(16), ctypes.c_void_p(16), None, None, 0, 0, None, None,
                           None, 0, ctypes.byref(st), None) == 3
+    # counter-based uniforms: negative length, missing output; an empty stream enqueues nothing
+    assert lib.dsv_philox_uniforms(0, 0, 0, 0, -1, ctypes.c_void_p(16), None) == 1
+    assert lib.dsv_philox_uniforms(0, 0, 0, 0, 8, None, None) == 1
+    assert lib.dsv_philox_uniforms(0, 0, 0, 0, 0, None, None) == 0
     assert st.value == 0
 
 
