@@ -1,6 +1,7 @@
 """HIP-graph capture of the calls beyond the greedy step: budget allocator + pack, verification
 attention through a cache map, a head_dim-256 launch with head groups and two waves per head,
-the sampling-mode verifier and the draft confidence features.  One captured graph holds all
+the sampling-mode verifier on uniforms drawn in the graph by the counter-based generator, and
+the draft confidence features.  One captured graph holds all
 of them; three replays, with eager work and synchronisation between them, reproduce the eager
 outputs bit for bit."""
 import numpy as np
@@ -48,8 +49,8 @@ def test_next_rows_graph_capture_replays_match_eager():
     sp = dsv.pack_slots(to_dev(sk), to_dev(np.zeros(4, np.int32)), to_dev(np.zeros(4, np.int64)),
                         to_dev(sbt), int(sk.sum()) + 2, st)
     slogits = to_dev(slog)
-    u_acc = to_dev(wl.uniforms(g, slog.shape[0]))
-    u_draw = to_dev(wl.uniforms(g, 4))
+    u_acc = torch.empty(slog.shape[0], dtype=torch.float32, device=DEV)
+    u_draw = torch.empty(4, dtype=torch.float32, device=DEV)
     skd = to_dev(sk)
     sws = torch.zeros(dsv.accept_sample_workspace_bytes(4, slog.shape[0], 3000), dtype=torch.uint8, device=DEV)
     sout = {}
@@ -70,6 +71,8 @@ def test_next_rows_graph_capture_replays_match_eager():
                            k_new=d2["k_new"], v_new=d2["v_new"], slot_cache_loc=packed2["slot_cache_loc"],
                            kv_chunk=256, workspace=ws2)
         dsv.verify_attn_call(a2)
+        dsv.philox_uniforms(0xABC, 0, slog.shape[0], out=u_acc)
+        dsv.philox_uniforms(0xABC, (slog.shape[0] + 3) // 4, 4, out=u_draw)
         dsv.accept_sample(n_bs=4, W=16, status=st, target_logits=slogits, temperature=0.8,
                           slot_tok=sp["slot_tok"], offsets=sp["offsets"], k=skd, u_accept=u_acc,
                           u_draw=u_draw, out=sout, workspace=sws)
@@ -78,7 +81,7 @@ def test_next_rows_graph_capture_replays_match_eager():
     calls()
     torch.cuda.synchronize()
     results = lambda: [alloc[k] for k in sorted(alloc)] + [out, lse, out2, lse2] + \
-        [sout[k] for k in sorted(sout)] + [fout]  # noqa: E731
+        [u_acc, u_draw] + [sout[k] for k in sorted(sout)] + [fout]  # noqa: E731
     eager = [t.clone() for t in results()]
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
