@@ -2,9 +2,12 @@
 
 A step is one pass of the hot path over the full-width verification workload (8 requests x
 16 slots = 128 packed slots, 32 query / 8 KV heads, head_dim 128, context 8192, bf16;
-target logits [128, 151936] fp32): dsv_pack_slots -> dsv_verify_attn (this step's candidate
-KV written at the packed cache references, split-KV attention, merge) -> dsv_accept
-(per-slot argmax, longest exact prefix, bonus token).
+target logits [128, 151936] fp32): dsv_pack_verify_attn (the packer fused into the
+verification launch: offsets and slot fields, this step's candidate KV written at the packed
+cache references, split-KV attention; then the merge) -> dsv_accept (per-slot argmax, longest
+exact prefix, bonus token).  The same step with the packer as its own launch (dsv_pack_slots
+-> dsv_verify_attn -> dsv_accept) is replayed beside it and reported as
+`separate_pack_ms_per_step`.
 
 Inputs are resident in HBM before timing.  To keep the 256 MiB Infinity Cache from serving
 the KV stream, the step rotates over enough copies of the KV pool and logits to exceed 1 GB
@@ -473,6 +476,12 @@ def main():
                          dtype=torch.uint8, device=dev)
 
     def step(s, arg_list):
+        dsv.pack_verify_attn(arg_list[s], tok, out=packed)
+        dsv.accept(n_bs=c["n_bs"], W=W, status=status, target_logits=pools[s % len(pools)][2],
+                   slot_tok=packed["slot_tok"], offsets=packed["offsets"], k=k, out=acc_out,
+                   workspace=acc_ws)
+
+    def step_separate_pack(s, arg_list):
         dsv.pack_slots(k, ctx, base, tok, m_bs, status, out=packed)
         dsv.verify_attn_call(arg_list[s])
         dsv.accept(n_bs=c["n_bs"], W=W, status=status, target_logits=pools[s % len(pools)][2],
@@ -505,6 +514,16 @@ def main():
         graphs[0].replay()
         # timed region 2: the same steps replayed as HIP graphs
         total_ms = timed(lambda: [g.replay() for g in graphs])
+        # the step with the packer as its own launch, for comparison (not the reported value)
+        sep_graphs = []
+        for s in range(args.warmup, n_total):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step_separate_pack(s, plain_args)
+            sep_graphs.append(g)
+        sep_graphs[0].replay()
+        sep_ms = timed(lambda: [g.replay() for g in sep_graphs])
+        del sep_graphs
     st = int(status.item())
     if st != 0:
         print(json.dumps({"error": f"device status {st}"}))
@@ -538,8 +557,8 @@ def main():
             "workload": "full-width verify: 8 requests x 16 slots (128 packed), 32 query / 8 KV "
                         "heads, head_dim 128, context 8192, bf16; fp32 logits [128, 151936]",
             "n_requests": 8, "slots": slots, "context": 8192, "hq": 32, "hkv": 8, "head_dim": 128,
-            "vocab": 151936, "step": "pack + verify attention (incl. candidate KV write, split-KV "
-                                      "merge) + accept",
+            "vocab": 151936, "step": "pack fused into verify attention (incl. candidate KV write, "
+                                      "split-KV merge) + accept",
             "launch": "HIP graph per step" if args.graph else "direct calls",
         },
         "roofline": {
@@ -556,6 +575,8 @@ def main():
         "attn_kernel_slots_per_s": slots / (attn_avg_ms * 1e-3),
         "direct_call_ms_per_step": direct_ms / args.steps,
     }
+    if args.graph:
+        res["separate_pack_ms_per_step"] = sep_ms / args.steps
     # practical read ceiling of this machine: a plain streaming read of the same KV bytes
     lib = dsv._lib.load()
     sink = torch.zeros(1, dtype=torch.float32, device=dev)

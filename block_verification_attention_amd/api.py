@@ -147,7 +147,8 @@ def attn_args(q, k_pool, v_pool, offsets, k, ctx_len, kv_base, *, W: int, max_ct
         a.n_bs = k.shape[0]
         a.m_bs = q.shape[0]
         a.W = W
-        a.offsets, a.k, a.ctx_len, a.kv_base = (t.data_ptr() for t in (offsets, k, ctx_len, kv_base))
+        a.offsets = offsets.data_ptr() if offsets is not None else None  # None: pack_verify_attn
+        a.k, a.ctx_len, a.kv_base = (t.data_ptr() for t in (k, ctx_len, kv_base))
         a.slot_cache_loc = slot_cache_loc.data_ptr() if slot_cache_loc is not None else None
         a.q = q.data_ptr()
         a.k_new = k_new.data_ptr() if k_new is not None else None
@@ -187,6 +188,36 @@ def verify_attn_workspace_bytes(args: AttnArgs) -> int:
 
 def verify_attn_call(args: AttnArgs, stream=None):
     check(_lib.load().dsv_verify_attn(ctypes.byref(args), _stream(stream)), "dsv_verify_attn")
+
+
+def pack_verify_attn(args: AttnArgs, block_tokens, out=None, stream=None) -> dict:
+    """dsv_pack_verify_attn: the packer fused into the verification launch.  `args` as for
+    verify_attn_call (its offsets and slot_cache_loc are ignored); block_tokens [n_bs, W]
+    int32.  Returns the packer's outputs (as pack_slots; `out` may supply them)."""
+    lib = _lib.load()
+    dev = block_tokens.device
+    _need(block_tokens, torch.int32, "block_tokens", dev)
+    n_bs, m_bs = int(args.n_bs), int(args.m_bs)
+    if tuple(block_tokens.shape) != (n_bs, int(args.W)):
+        raise ValueError("block_tokens: expected [n_bs, W]")
+    if out is None:
+        out = dict(
+            offsets=torch.empty(n_bs + 1, dtype=torch.int32, device=dev),
+            slot_req=torch.empty(m_bs, dtype=torch.int32, device=dev),
+            slot_tok=torch.empty(m_bs, dtype=torch.int32, device=dev),
+            slot_pos=torch.empty(m_bs, dtype=torch.int32, device=dev),
+            slot_cache_loc=torch.empty(m_bs, dtype=torch.int64, device=dev),
+        )
+    for key, dt, n in (("offsets", torch.int32, n_bs + 1), ("slot_req", torch.int32, m_bs),
+                       ("slot_tok", torch.int32, m_bs), ("slot_pos", torch.int32, m_bs),
+                       ("slot_cache_loc", torch.int64, m_bs)):
+        _need(out[key], dt, key, dev)
+        if out[key].numel() < n:
+            raise ValueError(f"{key}: expected at least {n} elements")
+    check(lib.dsv_pack_verify_attn(ctypes.byref(args), _ptr(block_tokens), _ptr(out["offsets"]),
+                                   _ptr(out["slot_req"]), _ptr(out["slot_tok"]), _ptr(out["slot_pos"]),
+                                   _ptr(out["slot_cache_loc"]), _stream(stream)), "dsv_pack_verify_attn")
+    return out
 
 
 def verify_attn(q, k_pool, v_pool, offsets, k, ctx_len, kv_base, *, W: int, max_ctx: int,

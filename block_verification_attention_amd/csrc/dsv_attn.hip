@@ -78,6 +78,11 @@ struct AttnParams {
   // token-granular cache map of the verification set (null: contiguous segments)
   const int32_t *kv_index;
   int64_t kv_index_stride;
+  // packer fused into the verification launch (pk_offsets non-null): the kernel forms the
+  // offsets itself and writes the packer's outputs; `offsets` then points at pk_offsets
+  const int32_t *pk_tokens;
+  int32_t *pk_offsets, *pk_req, *pk_tok, *pk_pos;
+  int64_t *pk_loc;
 };
 
 // Checks request i of the verification set; on success returns 0 and its fields.
@@ -200,7 +205,9 @@ constexpr float kRescaleSlack = 8.0f;
 // ---------------------------------------------------------------------------
 template <int D, int NW>
 constexpr int waves_per_eu_hint() {
-  // small workgroups get the whole register file; 3..8 waves are asked to fit 2 waves/SIMD
+  // small workgroups get the whole register file; 3..8 waves are asked to fit 2 waves/SIMD,
+  // and exactly 2 (a third wave per SIMD cannot host another workgroup of this size, and
+  // tighter register budgets cost the tile loop its loads in flight)
   return (NW <= 2 || (D == 256 && NW <= 4)) ? 1 : (NW <= 8 ? 2 : 1);
 }
 
@@ -208,7 +215,7 @@ constexpr int waves_per_eu_hint() {
 // output columns (both compute the head's scores), so that a wave holds D / (4 DS) output
 // registers per lane.
 template <int D, int NW, bool PF, int TILE, int HV, bool MAP, int DS = 1>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_per_eu_hint<D, NW>()))) void attn_bf16_kernel(AttnParams p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_per_eu_hint<D, NW>(), waves_per_eu_hint<D, NW>() == 2 ? 2 : 10))) void attn_bf16_kernel(AttnParams p) {
   constexpr int RPC = 1024 / (2 * D);        // rows per 1 KB wave load
   constexpr int NCK = TILE / RPC;            // wave loads per tensor per tile
   constexpr int NP = 2 * NCK * HV;           // wave loads per stage (HV tiles of K and V)
@@ -269,15 +276,65 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     split = t / p.n_bs;
     const int h0 = g * p.G + hg * p.GW;
     h = h0 + wh;
-    if (i == 0 && split == 0) {
-      int end = p.offsets[p.n_bs];
+    int ki, bad, end;
+    if (p.pk_offsets) {
+      // Packer fused into this launch (the flat-buffer packer's rule, as dsv_pack_slots): the
+      // effective lengths are k_r for well-formed requests, else 0, and all 0 when they sum
+      // above m_bs; offset_i is their exclusive sum.  Every wavefront forms its request's
+      // offset and the total itself (lanes over the requests, shuffle sums: no barrier), with
+      // the request's own fields loaded alongside; the first workgroup of each request writes
+      // that request's packer outputs, request 0's also the tail.
+      c = p.ctx_len[i];
+      kb = p.kv_base[i];
+      const int k_i = p.k[i];
+      int s_all = 0, s_before = 0;
+      for (int r0 = 0; r0 < p.n_bs; r0 += kWave) {
+        const int r = r0 + lane;
+        const int e = r < p.n_bs ? pack_effective_length(p.k[r], p.ctx_len[r], p.kv_base[r], p.W) : 0;
+        s_all += e;
+        s_before += r < i ? e : 0;
+      }
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) {
+        s_all += __shfl_xor(s_all, d);
+        s_before += __shfl_xor(s_before, d);
+      }
+      const bool drop_all = s_all > p.m_bs;
+      ki = drop_all ? 0 : pack_effective_length(k_i, c, kb, p.W);
+      off = drop_all ? 0 : s_before;
+      end = drop_all ? 0 : s_all;
+      if (split == 0 && g == 0 && hg == 0) {
+        for (int j = tid; j < ki; j += NW * 64) {  // slot off + j: candidate j of request i
+          p.pk_req[off + j] = i;
+          p.pk_tok[off + j] = p.pk_tokens[(int64_t)i * p.W + j];
+          p.pk_pos[off + j] = c + j;
+          p.pk_loc[off + j] = kb + c + j;
+        }
+        if (tid == 0) {
+          p.pk_offsets[i] = off;
+          if (!pack_request_ok(k_i, c, kb, p.W)) status_or(p.status, DSV_STATUS_BAD_REQUEST);
+          if (i == 0) {
+            p.pk_offsets[p.n_bs] = end;
+            if (drop_all) status_or(p.status, DSV_STATUS_BUDGET);
+          }
+        }
+        if (i == 0)
+          for (int sl = end + tid; sl < p.m_bs; sl += NW * 64) {
+            p.pk_req[sl] = -1;
+            p.pk_tok[sl] = 0;
+            p.pk_pos[sl] = 0;
+            p.pk_loc[sl] = -1;
+          }
+      }
+      bad = ki > 0 && kb + c + ki > p.pool_rows ? DSV_STATUS_POOL : 0;
+    } else {
+      end = p.offsets[p.n_bs];
       end = end < 0 ? 0 : (end > p.m_bs ? p.m_bs : end);
-      zero_rows_bf16<D>(static_cast<uint16_t *>(p.out), p.lse, p.hq, end, p.m_bs, h0,
-                        min(p.GW, p.G - hg * p.GW),
-                        tid, NW * 64);
+      bad = verify_request(p, i, ki, off, c, kb);
     }
-    int ki;
-    const int bad = verify_request(p, i, ki, off, c, kb);
+    if (i == 0 && split == 0)
+      zero_rows_bf16<D>(static_cast<uint16_t *>(p.out), p.lse, p.hq, end, p.m_bs, h0,
+                        min(p.GW, p.G - hg * p.GW), tid, NW * 64);
     if (bad) {
       if (split == 0) {
         if (tid == 0 && g == 0 && hg == 0) status_or(p.status, bad);
@@ -735,7 +792,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
         const int isv = e / (nrows * C16);
         const int rem = e % (nrows * C16);
         const int j = rem / C16, cc = rem % C16;
-        const int64_t loc = p.slot_cache_loc[off + j];
+        const int64_t loc = p.pk_offsets ? kb + c + j : p.slot_cache_loc[off + j];
         if (loc < 0 || loc >= p.pool_rows) {
           status_or(p.status, DSV_STATUS_POOL);
           continue;
@@ -826,7 +883,16 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   if (i >= p.n_bs) return;
   int ki, off, c;
   int64_t kb;
-  if (verify_request(p, i, ki, off, c, kb) || j >= ki) return;
+  if (p.pk_offsets) {
+    // fused packer: the effective length is the difference of the offsets it wrote
+    off = p.offsets[i];
+    ki = p.offsets[i + 1] - off;
+    c = p.ctx_len[i];
+    kb = p.kv_base[i];
+    if (j >= ki || kb + c + ki > p.pool_rows) return;
+  } else if (verify_request(p, i, ki, off, c, kb) || j >= ki) {
+    return;
+  }
   const int S = verify_splits(p, c + ki);
   if (S <= 1) return;
   const int64_t plane = (int64_t)p.m_bs * p.hq;
@@ -1216,7 +1282,16 @@ extern "C" size_t dsv_verify_attn_workspace_bytes(const dsv_attn_args *a) {
   return pl.ws_o + pl.ws_lse;
 }
 
-extern "C" dsv_status dsv_verify_attn(const dsv_attn_args *a, hipStream_t stream) {
+namespace dsv {
+// Outputs of the packer when it is fused into the verification launch.
+struct PackOut {
+  const int32_t *block_tokens;
+  int32_t *offsets, *slot_req, *slot_tok, *slot_pos;
+  int64_t *slot_cache_loc;
+};
+}  // namespace dsv
+
+static dsv_status verify_attn_impl(const dsv_attn_args *a, const dsv::PackOut *po, hipStream_t stream) {
   using namespace dsv;
   if (!a || !a->status) return DSV_ERR_INVALID_ARG;
   if (a->dtype != DSV_BF16 && a->dtype != DSV_F32) return DSV_ERR_UNSUPPORTED;
@@ -1234,10 +1309,10 @@ extern "C" dsv_status dsv_verify_attn(const dsv_attn_args *a, hipStream_t stream
   const bool prefill = a->n_pf > 0;
   if (verify) {
     if (a->W < 1 || a->W > DSV_MAX_W || a->max_ctx < 0) return DSV_ERR_INVALID_ARG;
-    if (!a->offsets || !a->k || !a->ctx_len || !a->kv_base || !a->q || !a->out)
+    if ((!a->offsets && !po) || !a->k || !a->ctx_len || !a->kv_base || !a->q || !a->out)
       return DSV_ERR_INVALID_ARG;
     if ((a->k_new == nullptr) != (a->v_new == nullptr)) return DSV_ERR_INVALID_ARG;
-    if (a->k_new && !a->slot_cache_loc) return DSV_ERR_INVALID_ARG;
+    if (a->k_new && !a->slot_cache_loc && !po) return DSV_ERR_INVALID_ARG;
     if (a->kv_chunk < 0 || a->kv_chunk % kTileKV) return DSV_ERR_INVALID_ARG;
     if (a->kv_index && a->kv_index_stride < 1) return DSV_ERR_INVALID_ARG;
   }
@@ -1276,11 +1351,19 @@ extern "C" dsv_status dsv_verify_attn(const dsv_attn_args *a, hipStream_t stream
   p.n_bs = a->n_bs;
   p.m_bs = a->m_bs;
   p.W = a->W;
-  p.offsets = a->offsets;
+  p.offsets = po ? po->offsets : a->offsets;
   p.k = a->k;
   p.ctx_len = a->ctx_len;
   p.kv_base = a->kv_base;
-  p.slot_cache_loc = a->slot_cache_loc;
+  p.slot_cache_loc = po ? po->slot_cache_loc : a->slot_cache_loc;
+  if (po) {
+    p.pk_tokens = po->block_tokens;
+    p.pk_offsets = po->offsets;
+    p.pk_req = po->slot_req;
+    p.pk_tok = po->slot_tok;
+    p.pk_pos = po->slot_pos;
+    p.pk_loc = po->slot_cache_loc;
+  }
   p.q = a->q;
   p.k_new = a->k_new;
   p.v_new = a->v_new;
@@ -1376,4 +1459,21 @@ extern "C" dsv_status dsv_verify_attn(const dsv_attn_args *a, hipStream_t stream
     }
   }
   return DSV_OK;
+}
+
+extern "C" dsv_status dsv_verify_attn(const dsv_attn_args *a, hipStream_t stream) {
+  return verify_attn_impl(a, nullptr, stream);
+}
+
+extern "C" dsv_status dsv_pack_verify_attn(const dsv_attn_args *a, const int32_t *block_tokens,
+                                           int32_t *offsets, int32_t *slot_req, int32_t *slot_tok,
+                                           int32_t *slot_pos, int64_t *slot_cache_loc,
+                                           hipStream_t stream) {
+  // the verification set in bf16 over contiguous segments, with the packer's outputs given
+  if (!a || a->dtype != DSV_BF16 || a->n_bs < 1 || a->kv_index) return a ? DSV_ERR_UNSUPPORTED : DSV_ERR_INVALID_ARG;
+  if (!block_tokens || !offsets || !slot_req || !slot_tok || !slot_pos || !slot_cache_loc)
+    return DSV_ERR_INVALID_ARG;
+  if (a->m_bs < 0 || a->W < 1 || a->W > DSV_MAX_W) return DSV_ERR_INVALID_ARG;
+  const dsv::PackOut po{block_tokens, offsets, slot_req, slot_tok, slot_pos, slot_cache_loc};
+  return verify_attn_impl(a, &po, stream);
 }

@@ -104,6 +104,40 @@ __device__ __forceinline__ void status_or(int32_t *status, int32_t bits) {
   if (status) atomicOr(status, bits);
 }
 
+// Flat-buffer packer rule (DScale Sec. III-C, Fig. 6): a request is well formed when its length
+// lies in [0, W] and its context and segment base are not negative; its effective length is
+// then k, else 0 (it takes no slots).  Offsets are the exclusive sums of effective lengths.
+__device__ __forceinline__ bool pack_request_ok(int k, int ctx, int64_t kv_base, int W) {
+  return k >= 0 && k <= W && ctx >= 0 && kv_base >= 0;
+}
+__device__ __forceinline__ int pack_effective_length(int k, int ctx, int64_t kv_base, int W) {
+  return pack_request_ok(k, ctx, kv_base, W) ? k : 0;
+}
+
+// Writes the slots [off, off + k) of request i (k <= W <= DSV_MAX_W): the request's tokens
+// are loaded together first, so the writes wait for one memory round trip, not one per slot.
+__device__ __forceinline__ void write_request_slots(int i, int k, int off, int W, int c, int64_t kb,
+                                                    const int32_t *__restrict__ block_tokens,
+                                                    int32_t *__restrict__ slot_req,
+                                                    int32_t *__restrict__ slot_tok,
+                                                    int32_t *__restrict__ slot_pos,
+                                                    int64_t *__restrict__ slot_cache_loc) {
+  int32_t tok[DSV_MAX_W];
+#pragma unroll
+  for (int j = 0; j < DSV_MAX_W; ++j) tok[j] = j < k ? block_tokens[(int64_t)i * W + j] : 0;
+#pragma unroll
+  for (int j = 0; j < DSV_MAX_W; ++j) {
+    if (j < k) {
+      const int s = off + j;
+      slot_req[s] = i;
+      slot_tok[s] = tok[j];
+      slot_pos[s] = c + j;
+      slot_cache_loc[s] = kb + c + j;
+    }
+  }
+}
+
+
 }  // namespace dsv
 
 // Host-side launch check: returns DSV_ERR_HIP from the enclosing function on failure.

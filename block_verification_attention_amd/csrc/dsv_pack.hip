@@ -29,29 +29,6 @@ __device__ __forceinline__ int64_t wave_inclusive_scan(int64_t v, int lane) {
 // One workgroup of NT threads (a multiple of 64, at most 1024).  Thread t owns the contiguous
 // run of requests [t * per, (t + 1) * per); the per-thread sums are scanned with wavefront
 // scans and one cross-wave pass, so the scan costs two barriers.
-// Writes the slots [off, off + k) of request i (k <= W <= DSV_MAX_W): the request's tokens
-// are loaded together first, so the writes wait for one memory round trip, not one per slot.
-__device__ __forceinline__ void write_request_slots(int i, int k, int off, int W, int c, int64_t kb,
-                                                    const int32_t *__restrict__ block_tokens,
-                                                    int32_t *__restrict__ slot_req,
-                                                    int32_t *__restrict__ slot_tok,
-                                                    int32_t *__restrict__ slot_pos,
-                                                    int64_t *__restrict__ slot_cache_loc) {
-  int32_t tok[DSV_MAX_W];
-#pragma unroll
-  for (int j = 0; j < DSV_MAX_W; ++j) tok[j] = j < k ? block_tokens[(int64_t)i * W + j] : 0;
-#pragma unroll
-  for (int j = 0; j < DSV_MAX_W; ++j) {
-    if (j < k) {
-      const int s = off + j;
-      slot_req[s] = i;
-      slot_tok[s] = tok[j];
-      slot_pos[s] = c + j;
-      slot_cache_loc[s] = kb + c + j;
-    }
-  }
-}
-
 __global__ __launch_bounds__(kPackMaxThreads) void pack_slots_kernel(
     int n_bs, int W, int m_bs, const int32_t *__restrict__ k, const int32_t *__restrict__ ctx_len,
     const int64_t *__restrict__ kv_base, const int32_t *__restrict__ block_tokens,
@@ -62,20 +39,13 @@ __global__ __launch_bounds__(kPackMaxThreads) void pack_slots_kernel(
   const int per = (n_bs + nt - 1) / nt;
   const int lo = min(n_bs, t * per), hi = min(n_bs, lo + per);
 
-  // Effective length of request i: k_i if the request is well formed, else 0.
-  auto eff = [&](int i) -> int {
-    int ki = k[i];
-    bool ok = ki >= 0 && ki <= W && ctx_len[i] >= 0 && kv_base[i] >= 0;
-    return ok ? ki : 0;
-  };
+  auto eff = [&](int i) -> int { return pack_effective_length(k[i], ctx_len[i], kv_base[i], W); };
 
   int64_t local = 0;
   bool bad = false;
   for (int i = lo; i < hi; ++i) {
-    int ki = k[i];
-    bool ok = ki >= 0 && ki <= W && ctx_len[i] >= 0 && kv_base[i] >= 0;
-    bad |= !ok;
-    local += ok ? ki : 0;
+    bad |= !pack_request_ok(k[i], ctx_len[i], kv_base[i], W);
+    local += eff(i);
   }
   if (bad) status_or(status, DSV_STATUS_BAD_REQUEST);
   const int64_t incl = wave_inclusive_scan(local, lane);

@@ -257,6 +257,33 @@ size_t dsv_verify_attn_workspace_bytes(const dsv_attn_args *args);
 dsv_status dsv_verify_attn(const dsv_attn_args *args, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* dsv_pack_verify_attn -- the packer fused into the verification launch    */
+/*                                                                            */
+/* DScale Sec. III-C (Flat-buffer packer, Fig. 6) and Sec. III-D (verification */
+/* over the packed slots) in one kernel launch (plus the split merge): the    */
+/* same results as dsv_pack_slots(a->n_bs, a->W, a->m_bs, a->k, a->ctx_len,   */
+/* a->kv_base, block_tokens, offsets, slot_req, slot_tok, slot_pos,           */
+/* slot_cache_loc, a->status) followed by dsv_verify_attn(a) with those       */
+/* offsets and cache references, for well-formed requests, without the       */
+/* packer's separate launch: every verification workgroup forms its          */
+/* request's offset from the effective lengths itself.                        */
+/*                                                                            */
+/* a: as for dsv_verify_attn; a->offsets and a->slot_cache_loc are ignored    */
+/*   (the packer's outputs below take their place); bf16, contiguous          */
+/*   segments (a->kv_index null), at least one request.  The packer's         */
+/*   outputs: as dsv_pack_slots (offsets [n_bs + 1], slot fields [m_bs]).     */
+/* Requests that are malformed (k outside [0, W], a negative context or base) */
+/*   or all requests when their lengths sum above m_bs take no slots and get  */
+/*   no attention rows (DSV_STATUS_BAD_REQUEST / DSV_STATUS_BUDGET); rows     */
+/*   past offsets[n_bs] are zero, their lse -inf.                             */
+/* Errors  host: as dsv_verify_attn, DSV_ERR_UNSUPPORTED (fp32, a cache map,  */
+/*   no verification set), DSV_ERR_INVALID_ARG (a missing packer output).     */
+/* ------------------------------------------------------------------------ */
+dsv_status dsv_pack_verify_attn(const dsv_attn_args *args, const int32_t *block_tokens,
+                                int32_t *offsets, int32_t *slot_req, int32_t *slot_tok,
+                                int32_t *slot_pos, int64_t *slot_cache_loc, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* dsv_accept -- greedy prefix verifier, output builder and draft margin     */
 /*                                                                            */
 /* DScale Sec. III-D (Prefix verifier, greedy: a deterministic top-1 draft   */
