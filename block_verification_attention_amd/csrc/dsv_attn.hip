@@ -206,8 +206,9 @@ constexpr float kRescaleSlack = 8.0f;
 template <int D, int NW>
 constexpr int waves_per_eu_hint() {
   // small workgroups get the whole register file; 3..8 waves are asked to fit 2 waves/SIMD,
-  // and exactly 2 (a third wave per SIMD cannot host another workgroup of this size, and
-  // tighter register budgets cost the tile loop its loads in flight)
+  // and at head_dim 128 and 256 exactly 2 (a third wave per SIMD cannot host another
+  // workgroup of this size, and tighter register budgets cost the tile loop its loads in
+  // flight); head_dim-64 kernels may run more per SIMD
   return (NW <= 2 || (D == 256 && NW <= 4)) ? 1 : (NW <= 8 ? 2 : 1);
 }
 
@@ -215,7 +216,7 @@ constexpr int waves_per_eu_hint() {
 // output columns (both compute the head's scores), so that a wave holds D / (4 DS) output
 // registers per lane.
 template <int D, int NW, bool PF, int TILE, int HV, bool MAP, int DS = 1>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_per_eu_hint<D, NW>(), waves_per_eu_hint<D, NW>() == 2 ? 2 : 10))) void attn_bf16_kernel(AttnParams p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_per_eu_hint<D, NW>(), waves_per_eu_hint<D, NW>() == 2 && D >= 128 ? 2 : 10))) void attn_bf16_kernel(AttnParams p) {
   constexpr int RPC = 1024 / (2 * D);        // rows per 1 KB wave load
   constexpr int NCK = TILE / RPC;            // wave loads per tensor per tile
   constexpr int NP = 2 * NCK * HV;           // wave loads per stage (HV tiles of K and V)
