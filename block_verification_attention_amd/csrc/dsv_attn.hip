@@ -46,8 +46,10 @@ constexpr int kXcds = 8;     // dispatch places block b on XCD b % 8
 // Waves with at most this many 16-byte loads per tile stage two tiles in registers (more
 // would push the hot shapes past the register budget of two waves per SIMD).
 constexpr int kTwoSetMaxLoads = 4;
-constexpr int kPfWaves = 8;  // 8 waves x 16 rows = 128-row prefill tile
-constexpr int kPfRows = kPfWaves * 16;
+// Prefill: waves per workgroup, 16 query rows each (128-row tile; 64 rows at head_dim 256,
+// whose wave needs the whole register file for its 16 x 256 output and query fragments).
+constexpr int pf_waves(int D) { return D >= 256 ? 4 : 8; }
+constexpr int pf_rows(int D) { return pf_waves(D) * 16; }
 
 struct AttnParams {
   void *k_pool, *v_pool;
@@ -397,11 +399,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
       if (tid == 0 && b == 0 && h == 0) status_or(p.status, bad);
       return;
     }
-    row0 = b * kPfRows;
+    row0 = b * (NW * 16);
     if (row0 >= ql) return;
     nrows = ql;
     r_lo = 0;
-    r_hi = c + min(row0 + kPfRows, ql);
+    r_hi = c + min(row0 + NW * 16, ql);
     q_row0 = qs;
     qsrc = static_cast<const uint16_t *>(p.pf_q);
   }
@@ -1376,7 +1378,7 @@ static dsv_status verify_attn_impl(const dsv_attn_args *a, const dsv::PackOut *p
   p.ws_lse = pl.ws_o ? reinterpret_cast<float *>(static_cast<char *>(a->workspace) + pl.ws_o) : nullptr;
   p.n_pf = a->n_pf;
   p.pf_max_len = a->pf_max_len;
-  p.pf_blocks = prefill ? (a->pf_max_len + kPfRows - 1) / kPfRows : 0;
+  p.pf_blocks = prefill ? (a->pf_max_len + pf_rows(a->d) - 1) / pf_rows(a->d) : 0;
   p.pf_q_rows = a->pf_q_rows;
   p.pf_q_start = a->pf_q_start;
   p.pf_q_len = a->pf_q_len;
@@ -1408,9 +1410,9 @@ static dsv_status verify_attn_impl(const dsv_attn_args *a, const dsv::PackOut *p
     if (a->dtype == DSV_BF16) {
       const int grid = (int)((int64_t)p.pf_blocks * a->n_pf * a->hq);
       p.xcd_sib_pf = p.G > 1 && grid % (kXcds * p.G) == 0;
-      const bool ok = D == 64    ? launch_attn<64, kPfWaves, true>(p, grid, stream)
-                      : D == 128 ? launch_attn<128, kPfWaves, true>(p, grid, stream)
-                                 : launch_attn<256, kPfWaves, true>(p, grid, stream);
+      const bool ok = D == 64    ? launch_attn<64, pf_waves(64), true>(p, grid, stream)
+                      : D == 128 ? launch_attn<128, pf_waves(128), true>(p, grid, stream)
+                                 : launch_attn<256, pf_waves(256), true>(p, grid, stream);
       if (!ok) return DSV_ERR_HIP;
     } else {
       const int64_t grid = (int64_t)a->n_pf * a->pf_max_len * a->hq;
