@@ -42,9 +42,9 @@ PROFILED_KERNEL = "attn_bf16_kernel<128, 8, false, 64, 2, false, 1>"
 # WRITE_SIZE runs (profiles/attn_verify_cfg3_hbm_traffic.md, calibrated there against the
 # streaming-read probe and a pool copy), valid for the kernel source with this SHA-256 only.
 COUNTED_SOURCE = ("block_verification_attention_amd/csrc/dsv_attn.hip",
-                  "6b5dddd28450c1780588fdd17052b58226addbe1c20b1c0be278e20d1d74ff91")
-COUNTED_READ_BYTES = 270_341_844
-COUNTED_WRITE_BYTES = 11_068_395
+                  "db79e74996664b228c1c78093f2b55348367e1e1ac9a638c91f711055643fc32")
+COUNTED_READ_BYTES = 270_332_340
+COUNTED_WRITE_BYTES = 10_812_112
 
 
 def counted_traffic():
