@@ -266,7 +266,9 @@ dsv_status dsv_verify_attn(const dsv_attn_args *args, hipStream_t stream);
 /* slot_cache_loc, a->status) followed by dsv_verify_attn(a) with those       */
 /* offsets and cache references, for well-formed requests, without the       */
 /* packer's separate launch: every verification workgroup forms its          */
-/* request's offset from the effective lengths itself.                        */
+/* request's offset from the effective lengths itself (each reads the        */
+/* lengths of all n_bs requests, so the call suits batches of up to a few    */
+/* thousand requests; larger ones are better served by the separate calls).  */
 /*                                                                            */
 /* a: as for dsv_verify_attn; a->offsets and a->slot_cache_loc are ignored    */
 /*   (the packer's outputs below take their place); bf16, contiguous          */
