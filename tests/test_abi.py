@@ -61,6 +61,22 @@ def test_host_validation_without_gpu():
                           ctypes.c_void_p(16), ctypes.c_void_p(16), ctypes.c_void_p(16),
                           ctypes.c_void_p(16), ctypes.c_void_p(16), None, None, 0, 0, None, None,
                           None, 0, ctypes.byref(st), None) == 3
+    # fused packer + verification: fp32, a cache map, no requests or a missing packer output
+    # are refused before anything is enqueued
+    b = _lib.AttnArgs()
+    b.dtype, b.d, b.hq, b.hkv, b.n_bs, b.m_bs, b.W = 1, 128, 8, 2, 2, 8, 16
+    b.status = ctypes.addressof(st)
+    dummy = ctypes.c_void_p(16)
+    outs = [dummy] * 6
+    assert lib.dsv_pack_verify_attn(ctypes.byref(b), *outs, None) == 2    # fp32
+    b.dtype = 0
+    b.kv_index = 16
+    assert lib.dsv_pack_verify_attn(ctypes.byref(b), *outs, None) == 2    # cache map
+    b.kv_index = None
+    b.n_bs = 0
+    assert lib.dsv_pack_verify_attn(ctypes.byref(b), *outs, None) == 2    # no verification set
+    b.n_bs = 2
+    assert lib.dsv_pack_verify_attn(ctypes.byref(b), dummy, None, dummy, dummy, dummy, dummy, None) == 1
     # counter-based uniforms: negative length, missing output; an empty stream enqueues nothing
     assert lib.dsv_philox_uniforms(0, 0, 0, 0, -1, ctypes.c_void_p(16), None) == 1
     assert lib.dsv_philox_uniforms(0, 0, 0, 0, 8, None, None) == 1
