@@ -9,7 +9,8 @@ take minutes).  The oracle receives copies of only the KV segments it needs and 
 sampled outputs: every slot and head of three verification requests (the shortest and the
 longest context, and the one at the median) and 16 rows of every prefill request (the first,
 the last and 14 seeded ones).  The candidate K/V written into the pool are checked bit for
-bit at the packed cache references of all 60 requests."""
+bit at the packed cache references of all 60 requests.  The launch runs both as
+dsv_pack_slots + dsv_verify_attn and as dsv_pack_verify_attn (the packer fused into it)."""
 import numpy as np
 import pytest
 import torch
@@ -28,7 +29,8 @@ def _dev_normal(seed, shape, scale=0.5):
     return (torch.randn(shape, generator=g, device=DEV) * scale).to(torch.bfloat16)
 
 
-def test_config5_mixed_launch_sampled():
+@pytest.mark.parametrize("fused_pack", [False, True])
+def test_config5_mixed_launch_sampled(fused_pack):
     c = wl.config5(draw=False)
     hq, hkv, d, W = c["hq"], c["hkv"], c["d"], c["W"]
     n, m_bs, pool_rows = c["n_bs"], c["m_bs"], c["pool_rows"]
@@ -65,7 +67,11 @@ def test_config5_mixed_launch_sampled():
 
     st = dsv.new_status(DEV)
     kd, cd, bd = to_dev(c["k"]), to_dev(c["ctx_len"]), to_dev(c["kv_base"])
-    packed = dsv.pack_slots(kd, cd, bd, to_dev(c["block_tokens"]), m_bs, st)
+    tok = to_dev(c["block_tokens"])
+    packed = dsv.pack_slots(kd, cd, bd, tok, m_bs, st)
+    if fused_pack:  # the fused call must produce these outputs itself
+        for t in packed.values():
+            t.fill_(-3)
     pf_out = torch.full_like(pf_q, float("nan"))
     pf_lse = torch.full((pf_rows, hq), float("nan"), device=DEV)
     prefill = dsv.Prefill(q_start=to_dev(pf["q_start"]), q_len=to_dev(pf["q_len"]),
@@ -73,12 +79,21 @@ def test_config5_mixed_launch_sampled():
                           out=pf_out, max_len=pf["max_len"], lse=pf_lse)
     out = torch.full_like(q, float("nan"))
     lse = torch.full((m_bs, hq), float("nan"), device=DEV)
-    dsv.verify_attn(q, k_pool, v_pool, packed["offsets"], kd, cd, bd, W=W,
-                    max_ctx=int(c["ctx_len"].max()), status=st, out=out, lse=lse, k_new=k_new,
-                    v_new=v_new, slot_cache_loc=packed["slot_cache_loc"], prefill=prefill)
+    if fused_pack:
+        args = dsv.attn_args(q, k_pool, v_pool, None, kd, cd, bd, W=W, max_ctx=int(c["ctx_len"].max()),
+                             out=out, status=st, lse=lse, k_new=k_new, v_new=v_new, prefill=prefill)
+        ws = torch.empty(max(dsv.verify_attn_workspace_bytes(args), 256), dtype=torch.uint8, device=DEV)
+        args.workspace, args.workspace_bytes = ws.data_ptr(), ws.numel()
+        dsv.pack_verify_attn(args, tok, out=packed)
+    else:
+        dsv.verify_attn(q, k_pool, v_pool, packed["offsets"], kd, cd, bd, W=W,
+                        max_ctx=int(c["ctx_len"].max()), status=st, out=out, lse=lse, k_new=k_new,
+                        v_new=v_new, slot_cache_loc=packed["slot_cache_loc"], prefill=prefill)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     assert np.array_equal(packed["offsets"].cpu().numpy(), offs)
+    for key in ("slot_req", "slot_tok", "slot_pos", "slot_cache_loc"):
+        assert np.array_equal(packed[key].cpu().numpy(), ref_pack[key]), key
 
     # candidate K/V at the packed cache references, all requests, bit for bit
     loc = torch.as_tensor(ref_pack["slot_cache_loc"][:int(offs[-1])], device=DEV)
