@@ -223,7 +223,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
   constexpr int NCK = TILE / RPC;            // wave loads per tensor per tile
   constexpr int NP = 2 * NCK * HV;           // wave loads per stage (HV tiles of K and V)
   constexpr int QPW = (NP + NW - 1) / NW;    // wave loads per wave per stage (at most)
-  constexpr int RSETS = QPW <= kTwoSetMaxLoads ? 2 : 1;  // register sets (stages in flight besides LDS)
+  constexpr int RSETS = (!PF && QPW <= kTwoSetMaxLoads) ? 2 : 1;  // register sets (stages in flight besides LDS)
   constexpr int SUB_BYTES = 2 * TILE * D * 2;  // one tile of K and V
   constexpr int STAGE_BYTES = HV * SUB_BYTES;
   constexpr int NWH = NW / HV;               // waves per KV half
@@ -588,17 +588,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
   const bool wave_live = wave_row_lo < nrows && wave_has_heads;
   const float sl2 = p.scale_log2;
 
-  // One tile of ROWS (TILE, or 32 for the candidate block) KV rows at positions base.. from
-  // LDS stage STAGE; with MASK, positions at or past hi or past the row's last visible position
-  // are excluded.
-  auto compute_tile = [&](int base, int hi, auto stage_c, auto mask_c, auto rows_c) __attribute__((always_inline)) {
+  // S^T blocks of one tile from LDS stage STAGE: acc_s[kb][e] = raw score of KV row
+  // base + 16kb + 4lg + e for query row lq (KB = the tile's rows / 16)
+  auto tile_qk = [&](auto stage_c, auto &acc_s) __attribute__((always_inline)) {
     constexpr int STAGE = decltype(stage_c)::value;
-    constexpr bool MASK = decltype(mask_c)::value;
-    constexpr int ROWS = decltype(rows_c)::value;
-    constexpr int KB = ROWS / 16;  // 16-row score blocks
-    constexpr int KK = ROWS / 32;  // 32-row P.V steps
-    // S^T blocks: acc_s[kb][e] = raw score of KV row base + 16kb + 4lg + e for query row lq
-    f32x4 acc_s[KB];
+    constexpr int KB = std::extent<std::remove_reference_t<decltype(acc_s)>>::value;
 #pragma unroll
     for (int kbk = 0; kbk < KB; ++kbk) {
       acc_s[kbk] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -609,6 +603,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
         acc_s[kbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], acc_s[kbk], 0, 0, 0);
       }
     }
+  };
+  // Online softmax of those scores (positions at or past hi or past the row's last visible
+  // position masked with MASK) and P.V from the same stage.
+  auto tile_softmax_pv = [&](int base, int hi, auto stage_c, auto mask_c, auto &acc_s) __attribute__((always_inline)) {
+    constexpr int STAGE = decltype(stage_c)::value;
+    constexpr bool MASK = decltype(mask_c)::value;
+    constexpr int KB = std::extent<std::remove_reference_t<decltype(acc_s)>>::value;
+    constexpr int KK = KB / 2;  // 32-row P.V steps
     float mt = -INFINITY;  // this lane's maximum over its entries of the row
 #pragma unroll
     for (int kbk = 0; kbk < KB; ++kbk)
@@ -671,6 +673,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
       }
     }
   };
+  // One tile of ROWS (TILE, or 32 for the candidate block) KV rows at positions base.. from
+  // LDS stage STAGE; with MASK, positions at or past hi or past the row's last visible position
+  // are excluded.
+  auto compute_tile = [&](int base, int hi, auto stage_c, auto mask_c, auto rows_c) __attribute__((always_inline)) {
+    f32x4 acc_s[decltype(rows_c)::value / 16];
+    tile_qk(stage_c, acc_s);
+    tile_softmax_pv(base, hi, stage_c, mask_c, acc_s);
+  };
 
   // rows of this wave that can see any key of tile `base`; interior tiles skip the mask
   auto consume = [&](int stage_base, auto stage_c) __attribute__((always_inline)) {
@@ -728,6 +738,58 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
   // other stage, which every wave finished reading before the previous barrier, and reuses the
   // freed register set for tile t + 1 + RSETS.  One barrier per tile.
   Piece xa[QPW], xb[QPW];
+  if constexpr (PF) {
+    // Prefill: three LDS stages, so that a wave computes tile t + 1's Q.K products and then
+    // tile t's softmax and P.V (the softmax's VALU work issues while those MFMAs run) while
+    // tile t + 2 is stored into the third stage; one barrier per tile.  Tile t sits in stage
+    // t % 3 and its scores in buffer t % 2 (the loop is unrolled by 6).
+    constexpr int KB = TILE / 16;
+    f32x4 sa[KB], sb[KB];
+    auto live = [&](int t) __attribute__((always_inline)) {
+      return wave_live && r_lo + t * TILE <= c + wave_row_lo + 15;
+    };
+    if (n_tiles > 0) load_tile(r_lo, xa);
+    if (n_tiles > 1) load_tile(r_lo + TILE, xb);
+    if (n_tiles > 0) store_tile(xa, 0);
+    if (n_tiles > 1) store_tile(xb, 1);
+    if (n_tiles > 2) load_tile(r_lo + 2 * TILE, xa);
+    __syncthreads();
+    if (n_tiles > 0 && live(0)) tile_qk(std::integral_constant<int, 0>{}, sa);
+    auto iter = [&](int t, auto s_c, auto &cur, auto &nxt) __attribute__((always_inline)) {
+      constexpr int S = decltype(s_c)::value;
+      if (t + 1 < n_tiles && live(t + 1)) tile_qk(std::integral_constant<int, (S + 1) % 3>{}, nxt);
+      if (live(t)) {
+        const int base = r_lo + t * TILE;
+        if (base + TILE - 1 <= c + wave_row_lo && base + TILE <= t_hi)
+          tile_softmax_pv(base, t_hi, s_c, std::integral_constant<bool, false>{}, cur);
+        else
+          tile_softmax_pv(base, t_hi, s_c, std::integral_constant<bool, true>{}, cur);
+      }
+      if (t + 2 < n_tiles) {
+        if (t + 3 < n_tiles)
+          store_load_tile(xa, (S + 2) % 3, r_lo + (t + 3) * TILE);
+        else
+          store_tile(xa, (S + 2) % 3);
+      }
+      __syncthreads();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    for (int t = 0; t < n_tiles; t += 6) {
+      iter(t, I0{}, sa, sb);
+      if (t + 1 >= n_tiles) break;
+      iter(t + 1, I1{}, sb, sa);
+      if (t + 2 >= n_tiles) break;
+      iter(t + 2, I2{}, sa, sb);
+      if (t + 3 >= n_tiles) break;
+      iter(t + 3, I0{}, sb, sa);
+      if (t + 4 >= n_tiles) break;
+      iter(t + 4, I1{}, sa, sb);
+      if (t + 5 >= n_tiles) break;
+      iter(t + 5, I2{}, sb, sa);
+    }
+  }
   if constexpr (!PF) {
     if (has_cand) {
       // The candidate block is staged (into stage 1, which the loop first writes after a
@@ -750,7 +812,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
       __syncthreads();
     }
   }
-  if (!has_cand) {
+  if (!PF && !has_cand) {
     if (n_tiles > 0) load_tile(r_lo, xa);
     if constexpr (RSETS == 2) {
       if (n_tiles > 1) load_tile(r_lo + (HV * TILE), xb);
@@ -762,7 +824,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     }
     __syncthreads();
   }
-  for (int t = 0; t < n_tiles; t += 2) {
+  for (int t = 0; t < (PF ? 0 : n_tiles); t += 2) {
     consume(r_lo + t * (HV * TILE), std::integral_constant<int, 0>{});
     if (t + 1 < n_tiles) {
       if constexpr (RSETS == 2) {
@@ -1205,7 +1267,7 @@ static bool launch_attn_k(const AttnParams &p, int grid, hipStream_t s, hipEvent
   // split evenly over its waves (fewer, longer stages; otherwise the uneven piece pattern
   // spills)
   constexpr int TILE = (DS > 1 && (64 / (1024 / (2 * D))) % NW == 0) ? 64 : TileCfg<D>::TILE;
-  constexpr size_t shm = (size_t)2 * HV * 2 * TILE * D * sizeof(uint16_t);
+  constexpr size_t shm = (size_t)(PF ? 3 : 2) * HV * 2 * TILE * D * sizeof(uint16_t);
   auto kern = attn_bf16_kernel<D, NW, PF, TILE, HV, MAP, DS>;
   // once per kernel (idempotent), so that a captured call contains launches only
   static bool lds_limit_set = false;
