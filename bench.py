@@ -42,9 +42,9 @@ PROFILED_KERNEL = "attn_bf16_kernel<128, 8, false, 64, 2, false, 1>"
 # WRITE_SIZE runs (profiles/attn_verify_cfg3_hbm_traffic.md, calibrated there against the
 # streaming-read probe and a pool copy), valid for the kernel source with this SHA-256 only.
 COUNTED_SOURCE = ("block_verification_attention_amd/csrc/dsv_attn.hip",
-                  "db79e74996664b228c1c78093f2b55348367e1e1ac9a638c91f711055643fc32")
-COUNTED_READ_BYTES = 270_332_340
-COUNTED_WRITE_BYTES = 10_812_112
+                  "7854fabe0c01e8044aa74fadbab0f846152e6fa199938ad12799bd22f02db453")
+COUNTED_READ_BYTES = 270_334_286
+COUNTED_WRITE_BYTES = 10_978_304
 
 
 def counted_traffic():
@@ -417,8 +417,8 @@ def main():
                     help="launch each step's calls directly instead of replaying a captured HIP graph")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a "
-                                   "design note, not an implemented path", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "dsv runs on one GPU: splitting a step over several GPUs "
+                                   "is not implemented", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import numpy as np
