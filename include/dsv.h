@@ -407,10 +407,11 @@ dsv_status dsv_draft_features(int64_t rows, int32_t vocab, const float *draft_lo
 /*                                                                            */
 /* out[i] (f32, device) = (w_i >> 40) * 2^-24, w_i = 64-bit word i % 4 of    */
 /*   the Philox4x64-10 block at the 128-bit counter                           */
-/*   (counter_hi:counter_lo) + i / 4 (carried into counter_hi; the two high  */
-/*   counter words are 0) under the key (key1:key0).  Values are multiples   */
-/*   of 2^-24 in [0, 1).  A stream of n values consumes ceil(n / 4) counter  */
-/*   values, so consecutive calls can advance the counter by that much.      */
+/*   (counter_hi:counter_lo) + i / 4 (carried into counter_hi, the sum taken */
+/*   modulo 2^128; the two high counter words are 0) under the key           */
+/*   (key1:key0).  Values are multiples of 2^-24 in [0, 1).  A stream of n   */
+/*   values consumes ceil(n / 4) counter values, so consecutive calls can    */
+/*   advance the counter by that much.                                       */
 /* Errors  host: DSV_ERR_INVALID_ARG (n < 0, out null with n > 0, more than  */
 /*   2^31 workgroups), DSV_ERR_HIP.  n = 0 enqueues nothing.                  */
 /* ------------------------------------------------------------------------ */

@@ -79,6 +79,16 @@ def test_many_requests():
     _check_against_composed_and_oracle(c, tag="200 requests")
 
 
+def test_1500_requests():
+    # more requests than one 1024-thread block covers: every workgroup's prologue sums 1500
+    # effective lengths; short contexts keep the oracle quick
+    g = np.random.default_rng(6)
+    k = wl.lengths_geometric_rescaled(g, 1500, 12000)
+    c = small_case(334, hq=8, hkv=2, d=64, k=tuple(int(x) for x in k),
+                   ctx=tuple(int(x) for x in g.integers(0, 120, 1500)))
+    _check_against_composed_and_oracle(c, tag="1500 requests")
+
+
 def test_malformed_requests_take_no_slots():
     c = small_case(340, hq=8, hkv=2, d=128, k=(4, 6, 3, 5, 2), ctx=(10, 20, 30, 40, 50))
     d = device_case(c)

@@ -15,7 +15,8 @@ import block_verification_attention_amd as dsv  # noqa: E402
 
 @pytest.mark.parametrize("key,counter,n", [(0, 0, 1), (1, 0, 4), (12345, 7, 1001),
                                            ((3 << 64) + 99, 2**64 - 2, 4096 + 3),
-                                           (2**128 - 1, 2**128 - 64, 250), (77, 5, 1 << 20)])
+                                           (2**128 - 1, 2**128 - 64, 250), (5, 2**128 - 8, 101),
+                                           (77, 5, 1 << 20)])
 def test_uniforms_bit_exact(key, counter, n):
     got = dsv.philox_uniforms(key, counter, n, device=DEV)
     torch.cuda.synchronize()

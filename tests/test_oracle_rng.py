@@ -33,6 +33,14 @@ def test_partial_block_is_a_prefix():
     assert np.array_equal(oracle.philox_raw(42, 1001, 12), full[4:])
 
 
+def test_counter_wraps_modulo_2_128():
+    # the block after counter 2^128 - 1 is the block at counter 0 (no carry into the high words)
+    key = 0x5A5A << 70
+    assert np.array_equal(oracle.philox_raw(key, 2**128 - 1, 8)[4:], oracle.philox_raw(key, 0, 4))
+    # the carry out of the low word reaches the high word: counter 2^64 - 1, then 2^64
+    assert np.array_equal(oracle.philox_raw(key, 2**64 - 1, 8)[4:], oracle.philox_raw(key, 2**64, 4))
+
+
 def test_uniforms_lattice_and_distribution():
     u = oracle.philox_uniforms(2024, 0, 1 << 20).astype(np.float64)
     assert u.min() >= 0.0 and u.max() < 1.0
