@@ -154,17 +154,22 @@ __global__ __launch_bounds__(kFtThreads) void feat_partial_kernel(
 #pragma unroll
       for (int u = 0; u < kFtLoads; ++u)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float e = f[u][q];
-          bad |= e != e;
-          bm = fmaxf(bm, e);
-        }
+        for (int q = 0; q < 4; ++q) bm = fmaxf(bm, f[u][q]);
       if (bm > m) raise(bm);
       if (m > -INFINITY) {
+        // a NaN logit turns S into NaN here (its weight is NaN), caught before a later
+        // maximum rescales S
 #pragma unroll
         for (int u = 0; u < kFtLoads; ++u)
 #pragma unroll
           for (int q = 0; q < 4; ++q) add1(f[u][q]);
+        bad |= S != S;
+      } else {
+        // no finite value yet on this lane: the block holds only -inf and NaN
+#pragma unroll
+        for (int u = 0; u < kFtLoads; ++u)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) bad |= f[u][q] != f[u][q];
       }
       // list: only lanes whose block maximum beats the threshold look further
       if (first) {

@@ -73,6 +73,25 @@ def test_features_bad_rows():
     assert np.array_equal(got[good][:, :16], ref[:, :16])
 
 
+def test_features_bad_rows_long():
+    # rows of many blocks: a NaN before a larger maximum that rescales the running sums, a
+    # NaN among -inf only, a NaN as the last logit; the good rows around them are unaffected
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((6, 100_000)).astype(np.float32)
+    x[1, 3] = np.nan
+    x[1, 95_000] = 50.0
+    x[2] = -np.inf
+    x[2, 40_000] = np.nan
+    x[3, -1] = np.nan
+    got, st = _gpu(x)
+    assert st & dsv.STATUS_NAN
+    for r in (1, 2, 3):
+        assert np.all(np.isnan(got[r])), r
+    good = [0, 4, 5]
+    ref = oracle.draft_features(x[good])
+    assert np.array_equal(got[good][:, :16], ref[:, :16])
+
+
 def test_features_host_errors():
     st = dsv.new_status(DEV)
     with pytest.raises(dsv.DsvError):
