@@ -84,6 +84,42 @@ def test_host_validation_without_gpu():
     assert st.value == 0
 
 
+def test_host_validation_next_rows_without_gpu():
+    """The allocator, the sampling verifier, the draft features and the read probe refuse
+    bad sizes and missing pointers before any HIP call; empty batches enqueue nothing."""
+    lib = _lib.load()
+    st = ctypes.c_int32(0)
+    sp = ctypes.addressof(st)
+    d = ctypes.c_void_p(16)
+    # allocator + pack: more than 1024 requests, W out of range, missing k, m_bs < m_live
+    alloc = lambda n_live, n_bs, W, m_live, m_bs, k=d: lib.dsv_allocate_pack(  # noqa: E731
+        n_live, n_bs, W, m_live, m_bs, d, d, d, d, k, d, d, d, d, d, d, sp, None)
+    assert alloc(4, 1025, 16, 8, 64) == 1
+    assert alloc(4, 8, 17, 8, 64) == 1
+    assert alloc(4, 8, 16, 8, 64, k=None) == 1
+    assert alloc(4, 8, 16, 65, 64) == 1
+    assert alloc(9, 8, 16, 8, 64) == 1
+    # sampling verifier: temperature not positive and finite, W out of range, missing output
+    samp = lambda n_bs, W, T, acc=d: lib.dsv_accept_sample(  # noqa: E731
+        n_bs, 64, W, 1000, d, T, d, d, d, d, d, acc, d, d, d, d, d, 1 << 20, sp, None)
+    for T in (0.0, -1.0, float("nan"), float("inf")):
+        assert samp(4, 16, T) == 1, T
+    assert samp(4, 0, 0.8) == 1
+    assert samp(4, 16, 0.8, acc=None) == 1
+    assert samp(0, 16, 0.8) == 0
+    # draft features: fewer than 16 logits, missing input, too small a workspace, no rows
+    assert lib.dsv_draft_features(4, 15, d, d, d, 1 << 20, sp, None) == 1
+    assert lib.dsv_draft_features(4, 4096, None, d, d, 1 << 20, sp, None) == 1
+    need = lib.dsv_draft_features_workspace_bytes(4, 4096)
+    assert lib.dsv_draft_features(4, 4096, d, d, d, need - 1, sp, None) == 3
+    assert lib.dsv_draft_features(0, 4096, None, None, None, 0, sp, None) == 0
+    # read probe: null, unaligned or shorter than 16 bytes
+    assert lib.dsv_probe_stream_read(None, 1 << 20, d, None) == 1
+    assert lib.dsv_probe_stream_read(ctypes.c_void_p(24), 1 << 20, d, None) == 1
+    assert lib.dsv_probe_stream_read(d, 15, d, None) == 1
+    assert st.value == 0
+
+
 def test_workspace_queries():
     lib = _lib.load()
     assert lib.dsv_accept_workspace_bytes(128, 151936, 0, 0, 0) > 0
