@@ -1,9 +1,10 @@
-"""The greedy accept step over a logits matrix past 2^31 elements (32-bit element offsets
-would wrap): 900 requests x 16 slots over a 151,936-token vocabulary, 14,400 x 151,936 fp32
-(8.75 GB), drawn on the device from a seeded generator.  Requests on both sides of the
-2^31-element boundary (and the one that straddles it) get planted accepted prefixes; the
+"""Logits sweeps over matrices past 2^31 elements (32-bit element offsets would wrap), drawn
+on the device from seeded generators.  The greedy accept step: 900 requests x 16 slots over a
+151,936-token vocabulary, 14,400 x 151,936 fp32 (8.75 GB); requests on both sides of the
+2^31-element boundary (and the one that straddles it) get planted accepted prefixes, and the
 oracle runs on copies of their rows and decides every per-slot argmax and per-request result
-of those requests."""
+of those requests.  The draft features: 8,700 positions x 248,320 tokens (8.6 GB), rows on both
+sides of the boundary and the row across it against the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -58,4 +59,30 @@ def test_accept_past_2_31_logits():
         assert np.array_equal(got["out_tokens"][i].cpu().numpy(), ref["out_tokens"][0]), i
         assert int(ref["accepted"][0]) >= a, (i, a)  # the planted prefix is accepted
     del logits
+    torch.cuda.empty_cache()
+
+
+def test_draft_features_past_2_31_logits():
+    # 8,700 draft positions x 248,320 tokens (2.16e9 fp32): rows on both sides of element 2^31
+    # and the row across it, checked against the oracle on copies of those rows
+    rows_n, vocab = 8_700, 248_320
+    assert rows_n * vocab > 1 << 31
+    across = (1 << 31) // vocab
+    sample = [0, across - 1, across, across + 1, rows_n - 1]
+    g = torch.Generator(device=DEV)
+    g.manual_seed(7202)
+    x = torch.empty((rows_n, vocab), dtype=torch.float32, device=DEV)
+    for r0 in range(0, rows_n, 1024):
+        x[r0:r0 + 1024].normal_(generator=g)
+    st = dsv.new_status(DEV)
+    f = dsv.draft_features(x, st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    got = f[torch.as_tensor(sample, device=DEV)].cpu().numpy()
+    ref = oracle.draft_features(x[torch.as_tensor(sample, device=DEV)].cpu().numpy())
+    assert np.array_equal(got[:, :16], ref[:, :16])
+    for c in (16, 17):
+        err = np.abs(got[:, c].astype(np.float64) - ref[:, c])
+        assert np.all(err <= 1e-4 * np.maximum(1.0, np.abs(ref[:, c]))), (c, err.max())
+    del x
     torch.cuda.empty_cache()
