@@ -3,7 +3,8 @@ would wrap): 2 KV heads x (2^24 + 40,000) rows x head_dim 128 per pool, 8.6 GB e
 requests' segments near the end of the pool, so both the row offset within a head and the
 second head's offset exceed 2^31 elements.  Only the rows the call reads are filled (seeded);
 the oracle receives compact copies of them.  The candidates' K/V written at their cache
-references are checked bit for bit, for both the separate and the fused packer."""
+references are checked bit for bit, for both the separate and the fused packer; a prefill set
+at the pool's end is checked row by row."""
 import numpy as np
 import pytest
 import torch
@@ -11,7 +12,7 @@ import torch
 pytestmark = pytest.mark.gpu
 
 import oracle  # noqa: E402
-from gpu_util import DEV, bits_of, compare_attn, to_dev  # noqa: E402
+from gpu_util import DEV, TOL, bits_of, compare_attn, to_dev, to_f64  # noqa: E402
 import block_verification_attention_amd as dsv  # noqa: E402
 
 POOL_ROWS = (1 << 24) + 40_000
@@ -78,5 +79,50 @@ def test_pool_offsets_past_2_31_elements(fused_pack):
     c = dict(n_bs=3, k=k, hq=HQ, dtype="bf16", m_bs=n)
     compare_attn(c, offs, out[:n], lse[:n], ref_o, ref_l, tag=f"large pool, fused {fused_pack}")
     assert torch.all(out[n:] == 0) and torch.all(torch.isneginf(lse[n:]))
+    del k_pool, v_pool
+    torch.cuda.empty_cache()
+
+
+def test_prefill_pool_offsets_past_2_31_elements():
+    # two prefill requests whose KV segments lie past element 2^31 of both heads; every row
+    # of both against the oracle on compact copies
+    q_len = np.array([300, 77], np.int32)
+    ctx = np.array([0, 150], np.int32)
+    base = np.array([POOL_ROWS - 20_000, POOL_ROWS - 400], np.int64)
+    q_start = np.array([0, 300], np.int32)
+    rows = int(q_len.sum())
+    g = torch.Generator(device=DEV)
+    g.manual_seed(7110)
+    k_pool = torch.empty((HKV, POOL_ROWS, D), dtype=torch.bfloat16, device=DEV)
+    v_pool = torch.empty((HKV, POOL_ROWS, D), dtype=torch.bfloat16, device=DEV)
+    for lo, n in zip(base, ctx + q_len):
+        k_pool[:, lo:lo + n] = _dev_normal(g, (HKV, int(n), D))
+        v_pool[:, lo:lo + n] = _dev_normal(g, (HKV, int(n), D))
+    q = _dev_normal(g, (rows, HQ, D))
+    kp_m = bits_of(torch.cat([k_pool[:, lo:lo + n] for lo, n in zip(base, ctx + q_len)], dim=1))
+    vp_m = bits_of(torch.cat([v_pool[:, lo:lo + n] for lo, n in zip(base, ctx + q_len)], dim=1))
+    kb_m = np.array([0, int(ctx[0] + q_len[0])], np.int64)
+
+    st = dsv.new_status(DEV)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((rows, HQ), float("nan"), device=DEV)
+    pf = dsv.Prefill(q_start=to_dev(q_start), q_len=to_dev(q_len), ctx_len=to_dev(ctx),
+                     kv_base=to_dev(base), q=q, out=out, max_len=int(q_len.max()), lse=lse)
+    args = dsv.attn_args(None, k_pool, v_pool, None, None, None, None, W=W, max_ctx=0, out=None,
+                         status=st, prefill=pf)
+    dsv.verify_attn_call(args)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    sel_req = [r for r in range(2) for _ in range(int(q_len[r]))]
+    sel_j = [j for r in range(2) for j in range(int(q_len[r]))]
+    ref_o, ref_l = oracle.prefill_attn(bits_of(q), kp_m, vp_m, q_start, q_len, ctx, kb_m, sel_req, sel_j)
+    go, gl = to_f64(out), to_f64(lse)
+    tol = TOL["bf16"]
+    assert np.all(np.isfinite(go))
+    assert np.abs(go - ref_o).max() <= tol["max_abs"], np.abs(go - ref_o).max()
+    for h in range(HQ):
+        rel = np.linalg.norm(go[:, h] - ref_o[:, h]) / np.linalg.norm(ref_o[:, h])
+        assert rel <= tol["rel_l2"], (h, rel)
+    assert np.abs(gl - ref_l).max() <= tol["lse"], np.abs(gl - ref_l).max()
     del k_pool, v_pool
     torch.cuda.empty_cache()
