@@ -3,7 +3,8 @@ would wrap): 2 KV heads x (2^24 + 40,000) rows x head_dim 128 per pool, 8.6 GB e
 requests' segments near the end of the pool, so both the row offset within a head and the
 second head's offset exceed 2^31 elements.  Only the rows the call reads are filled (seeded);
 the oracle receives compact copies of them.  The candidates' K/V written at their cache
-references are checked bit for bit, for both the separate and the fused packer; a prefill set
+references are checked bit for bit, for the separate and the fused packer and through a cache
+map (int32 entries naming rows past 2^24); a prefill set
 at the pool's end is checked row by row."""
 import numpy as np
 import pytest
@@ -23,15 +24,15 @@ def _dev_normal(g, shape):
     return (torch.randn(shape, generator=g, device=DEV) * 0.5).to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("fused_pack", [False, True])
-def test_pool_offsets_past_2_31_elements(fused_pack):
+@pytest.mark.parametrize("mode", ["separate", "fused", "cache_map"])
+def test_pool_offsets_past_2_31_elements(mode):
     assert (POOL_ROWS - 40_000) * D >= 1 << 31 and POOL_ROWS * D * HKV > 1 << 32
     k = np.array([16, 7, 1], np.int32)
     ctx = np.array([3000, 500, 1200], np.int32)
     base = np.array([POOL_ROWS - 39_000, POOL_ROWS - 30_000, POOL_ROWS - 1_300], np.int64)
     m_bs = int(k.sum()) + 5
     g = torch.Generator(device=DEV)
-    g.manual_seed(7100 + int(fused_pack))
+    g.manual_seed(7100 + ["separate", "fused", "cache_map"].index(mode))
     k_pool = torch.empty((HKV, POOL_ROWS, D), dtype=torch.bfloat16, device=DEV)
     v_pool = torch.empty((HKV, POOL_ROWS, D), dtype=torch.bfloat16, device=DEV)
     for lo, cx in zip(base, ctx):
@@ -51,12 +52,23 @@ def test_pool_offsets_past_2_31_elements(fused_pack):
     kd, cd, bd, td = to_dev(k), to_dev(ctx), to_dev(base), to_dev(tokens)
     out = torch.full_like(q, float("nan"))
     lse = torch.full((m_bs, HQ), float("nan"), device=DEV)
-    if fused_pack:
+    if mode == "fused":
         args = dsv.attn_args(q, k_pool, v_pool, None, kd, cd, bd, W=W, max_ctx=int(ctx.max()),
                              out=out, status=st, lse=lse, k_new=k_new, v_new=v_new)
         ws = torch.empty(max(dsv.verify_attn_workspace_bytes(args), 256), dtype=torch.uint8, device=DEV)
         args.workspace, args.workspace_bytes = ws.data_ptr(), ws.numel()
         packed = dsv.pack_verify_attn(args, td)
+    elif mode == "cache_map":
+        # identity map: position p of request i -> pool row base[i] + p (int32 entries)
+        stride = int((ctx + W).max())
+        idx = np.minimum(base[:, None] + np.arange(stride)[None, :], POOL_ROWS - 1).astype(np.int32)
+        packed = dsv.pack_slots(kd, cd, bd, td, m_bs, st)
+        a = dsv.attn_args(q, k_pool, v_pool, packed["offsets"], kd, cd, bd, W=W, max_ctx=int(ctx.max()),
+                          out=out, status=st, lse=lse, k_new=k_new, v_new=v_new,
+                          slot_cache_loc=packed["slot_cache_loc"], kv_index=to_dev(idx))
+        ws = torch.empty(max(dsv.verify_attn_workspace_bytes(a), 256), dtype=torch.uint8, device=DEV)
+        a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+        dsv.verify_attn_call(a)
     else:
         packed = dsv.pack_slots(kd, cd, bd, td, m_bs, st)
         dsv.verify_attn(q, k_pool, v_pool, packed["offsets"], kd, cd, bd, W=W, max_ctx=int(ctx.max()),
@@ -77,7 +89,7 @@ def test_pool_offsets_past_2_31_elements(fused_pack):
     ref_o, ref_l = oracle.verify_attn(bits_of(q[:n]), kp_m, vp_m, offs, k, ctx, kb_m,
                                       k_new=bits_of(k_new[:n]), v_new=bits_of(v_new[:n]))
     c = dict(n_bs=3, k=k, hq=HQ, dtype="bf16", m_bs=n)
-    compare_attn(c, offs, out[:n], lse[:n], ref_o, ref_l, tag=f"large pool, fused {fused_pack}")
+    compare_attn(c, offs, out[:n], lse[:n], ref_o, ref_l, tag=f"large pool, {mode}")
     assert torch.all(out[n:] == 0) and torch.all(torch.isneginf(lse[n:]))
     del k_pool, v_pool
     torch.cuda.empty_cache()
