@@ -368,12 +368,38 @@ def time_other_verify(dev, ev, iters: int = 20):
     return out
 
 
-def cpu_baseline(case, n_req_sample: int, min_seconds: float = 10.0, max_reps: int = 40):
+def cpu_model() -> str:
+    """The host CPU's model name (first processor of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(case, n_req_sample: int, min_seconds: float = 10.0, max_reps: int = 40,
+                 threads: int = 0):
     """The oracle (pack + fp64 attention + greedy accept) on the first n_req_sample requests,
     repeated until at least min_seconds of CPU work have run (at most max_reps passes); the
-    rate is slots over the mean time of a pass."""
+    rate is slots over the mean time of a pass.  threads > 0 runs the oracle on that many
+    threads (else its default: every core OpenMP offers)."""
     import numpy as np
 
+    import oracle
+
+    default_threads = oracle.threads()
+    if threads > 0:
+        oracle.set_threads(threads)
+    try:
+        return _cpu_baseline(case, n_req_sample, min_seconds, max_reps)
+    finally:
+        oracle.set_threads(default_threads)
+
+
+def _cpu_baseline(case, n_req_sample, min_seconds, max_reps):
     import oracle
 
     c = case
@@ -402,6 +428,8 @@ def cpu_baseline(case, n_req_sample: int, min_seconds: float = 10.0, max_reps: i
         "sample": f"{n_req_sample} of {c['n_bs']} requests ({m} slots), full context, fp64 "
                   f"attention over (request, KV head) units on {threads} threads; {reps} passes, "
                   f"{total:.1f} s in all, {dt:.2f} s per pass",
+        "cpu_model": cpu_model(),
+        "host_threads": os.cpu_count(),
     }
 
 
@@ -532,6 +560,21 @@ def main():
     if not np.array_equal(acc_out["accepted"].cpu().numpy(), c["planted_accepted"]):
         print(json.dumps({"error": "accepted lengths differ from the planted ones"}))
         sys.exit(1)
+    # the whole calls, by events recorded on the stream around each of back-to-back direct
+    # calls: dsv_verify_attn (attention kernel + split merge) and dsv_pack_verify_attn (the
+    # packer fused into it), with no kernel events attached
+    def time_calls(fn):
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(n_total)]
+        torch.cuda.synchronize()
+        for s in range(n_total):
+            pairs[s][0].record()
+            fn(s)
+            pairs[s][1].record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in pairs[args.warmup:]]))
+    call_ms = time_calls(lambda s: dsv.verify_attn_call(plain_args[s]))
+    fused_call_ms = time_calls(lambda s: dsv.pack_verify_attn(plain_args[s], tok, out=packed))
     attn_ms = [ev.elapsed_ms(main_ev[2 * s], main_ev[2 * s + 1]) for s in range(args.warmup, n_total)]
     ev.destroy(main_ev)
     attn_avg_ms = float(np.mean(attn_ms))
@@ -571,6 +614,11 @@ def main():
             "traffic": counted_traffic(),
             "algorithmic_bytes": kvb,
             "avg_launch_us": attn_avg_ms * 1e3,
+            # the dsv_verify_attn call (attention + split merge) and the fused packer call
+            "call_us": call_ms * 1e3,
+            "call_frac": kvb / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "fused_call_us": fused_call_ms * 1e3,
+            "fused_call_frac": kvb / (fused_call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         },
         "attn_kernel_slots_per_s": slots / (attn_avg_ms * 1e-3),
         "direct_call_ms_per_step": direct_ms / args.steps,
@@ -631,6 +679,9 @@ def main():
     res["other_verify"] = time_other_verify(dev, ev)
     if args.cpu_sample > 0:
         res["cpu_baseline"] = cpu_baseline(c, args.cpu_sample)
+        # the same oracle on one thread, over one request (16 slots)
+        one = cpu_baseline(c, 1, min_seconds=5.0, threads=1)
+        res["cpu_baseline"]["single_thread"] = {k: one[k] for k in ("value", "unit", "cores", "sample")}
     print(json.dumps(res))
 
 

@@ -90,6 +90,7 @@ def _load():
         lib.oracle_draft_features.argtypes = [i64, i64, P, P]
         lib.oracle_accept_sample.argtypes = [i32, i32, i32, i64, P, dbl] + [P] * 12
         lib.oracle_threads.argtypes = []
+        lib.oracle_set_threads.argtypes = [i32]
         lib.oracle_allocate.argtypes = [i32, i32, i32, i32, P, P, P]
         u64 = ctypes.c_uint64
         lib.oracle_philox_raw.argtypes = [u64, u64, u64, u64, i64, P]
@@ -124,6 +125,12 @@ def _elem_array(a):
 def threads() -> int:
     """OpenMP threads the oracle uses (OMP_NUM_THREADS, else all cores)."""
     return int(_load().oracle_threads())
+
+
+def set_threads(n: int) -> int:
+    """Runs the following oracle calls on n threads (results do not depend on the count);
+    returns the count in effect."""
+    return int(_load().oracle_set_threads(int(n)))
 
 
 # --------------------------------------------------------------------------

@@ -808,3 +808,15 @@ int oracle_threads(void) {
   return 1;
 #endif
 }
+
+/* Threads for the following calls (timing at a chosen thread count; results do not depend
+   on it).  Returns the count now in effect. */
+int oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+  return omp_get_max_threads();
+#else
+  (void)n;
+  return 1;
+#endif
+}

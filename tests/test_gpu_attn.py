@@ -41,7 +41,8 @@ def test_bf16_ragged(d_head, hq, hkv, kv_chunk):
     if (d_head, hq, hkv) == (256, 4, 4):
         pytest.skip("head_dim 256 with one query head per KV head: a GPU memory fault was seen "
                     "with an earlier schedule of direct global->LDS loads for this shape (that "
-                    "code is gone); its cause was never shown, so the case stays off the GPU")
+                    "code is gone); its cause was never shown, so the case stays off the GPU and "
+                    "the library refuses the grouping (DSV_ERR_UNSUPPORTED, checked on the CPU)")
     c = small_case(10 + d_head + hq, hq=hq, hkv=hkv, d=d_head,
                    k=(16, 5, 0, 11, 1, 16, 3), ctx=(700, 0, 40, 63, 64, 1000, 129))
     _run(c, kv_chunk=kv_chunk, tag=f"d{d_head} hq{hq} hkv{hkv} chunk{kv_chunk}")

@@ -67,6 +67,57 @@ def test_softmax_rows_sum_to_one():
         assert abs(p.sum() - 1.0) <= 1e-12 and np.all(p >= 0)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_softmax_probs_match_scipy(dtype):
+    """The materialised weights equal scipy's softmax of scale * K q (a library routine
+    independent of the oracle), for the default scale 1/sqrt(d) and for a given one, on
+    random rows and on a row where one planted key dominates."""
+    from scipy.special import softmax
+
+    r = np.random.default_rng(6)
+    conv = wl.to_bf16_bits if dtype == "bf16" else (lambda a: a.astype(np.float32))
+    for n, d, scale in ((1, 16, 0.0), (7, 32, 0.0), (40, 64, 0.37), (300, 128, 1.9)):
+        q = conv(r.standard_normal(d).astype(np.float32))
+        K = conv(r.standard_normal((n, d)).astype(np.float32))
+        p = oracle.softmax_probs(q, K, scale)
+        s = scale if scale > 0 else 1.0 / np.sqrt(d)
+        want = softmax(s * (_f64(K) @ _f64(q)))
+        assert np.allclose(p, want, rtol=1e-12, atol=1e-300), (n, d, scale)
+    # one key aligned with q and scaled up takes (almost) all the weight, at its own index
+    d, n, hot = 32, 50, 37
+    q = conv(np.ones(d, np.float32))
+    K = np.zeros((n, d), np.float32)
+    K[hot] = 1.0
+    p = oracle.softmax_probs(q, conv(K), 0.5)
+    assert int(np.argmax(p)) == hot and p[hot] > 1 - 1e-5
+    assert np.allclose(p[np.arange(n) != hot], np.exp(-16.0) / (np.exp(-16.0) * (n - 1) + 1.0), rtol=1e-12)
+
+
+def test_scatter_candidates_hand_built():
+    """Candidate K/V rows land exactly at their cache references, in every KV head; a -1
+    reference writes nothing; every other pool row and the inputs are unchanged.  Expected
+    pools are written out by hand."""
+    hkv, rows, d = 2, 6, 3
+    k_pool = np.arange(hkv * rows * d, dtype=np.float32).reshape(hkv, rows, d)  # value = index
+    v_pool = -k_pool
+    k_in, v_in = k_pool.copy(), v_pool.copy()
+    # three slots: slot 0 -> row 4, slot 1 -> tail placeholder (-1), slot 2 -> row 0
+    k_new = np.array([[[100, 101, 102], [110, 111, 112]],
+                      [[200, 201, 202], [210, 211, 212]],
+                      [[300, 301, 302], [310, 311, 312]]], np.float32)
+    v_new = k_new + 0.5
+    kp, vp = oracle.scatter_candidates(k_pool, v_pool, k_new, v_new, np.array([4, -1, 0], np.int64))
+    want_k = np.array([[[300, 301, 302], [3, 4, 5], [6, 7, 8], [9, 10, 11], [100, 101, 102], [15, 16, 17]],
+                       [[310, 311, 312], [21, 22, 23], [24, 25, 26], [27, 28, 29], [110, 111, 112], [33, 34, 35]]],
+                      np.float32)
+    want_v = np.array([[[300.5, 301.5, 302.5], [-3, -4, -5], [-6, -7, -8], [-9, -10, -11],
+                        [100.5, 101.5, 102.5], [-15, -16, -17]],
+                       [[310.5, 311.5, 312.5], [-21, -22, -23], [-24, -25, -26], [-27, -28, -29],
+                        [110.5, 111.5, 112.5], [-33, -34, -35]]], np.float32)
+    assert np.array_equal(kp, want_k) and np.array_equal(vp, want_v)
+    assert np.array_equal(k_pool, k_in) and np.array_equal(v_pool, v_in)  # copies, not in place
+
+
 def _sequence(c, i, off):
     """Request i's key/value sequence in position order (context rows, then k_new)."""
     b, cx, kk = int(c["kv_base"][i]), int(c["ctx_len"][i]), int(c["k"][i])
