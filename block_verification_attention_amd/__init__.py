@@ -25,6 +25,7 @@ from .api import (
     pack_verify_attn,
     verify_attn,
     verify_attn_call,
+    verify_attn_noalloc_call,
     verify_attn_workspace_bytes,
 )
 
@@ -33,7 +34,7 @@ __all__ = [
     "STATUS_PREFILL", "Prefill", "accept", "accept_sample", "accept_sample_workspace_bytes",
     "accept_workspace_bytes", "allocate_pack", "attn_args",
     "draft_features", "draft_features_workspace_bytes", "philox_uniforms", "new_status",
-    "pack_slots", "pack_verify_attn", "verify_attn", "verify_attn_call",
+    "pack_slots", "pack_verify_attn", "verify_attn", "verify_attn_call", "verify_attn_noalloc_call",
     "verify_attn_workspace_bytes",
 ]
 

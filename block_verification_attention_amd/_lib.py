@@ -78,6 +78,8 @@ def load():
     lib.dsv_verify_attn_workspace_bytes.restype = ctypes.c_size_t
     lib.dsv_verify_attn.argtypes = [ctypes.POINTER(AttnArgs), P]
     lib.dsv_verify_attn.restype = ctypes.c_int
+    lib.dsv_verify_attn_noalloc.argtypes = [ctypes.POINTER(AttnArgs), P]
+    lib.dsv_verify_attn_noalloc.restype = ctypes.c_int
     lib.dsv_pack_verify_attn.argtypes = [ctypes.POINTER(AttnArgs)] + [P] * 7
     lib.dsv_pack_verify_attn.restype = ctypes.c_int
     lib.dsv_accept_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]

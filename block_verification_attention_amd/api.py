@@ -190,6 +190,13 @@ def verify_attn_call(args: AttnArgs, stream=None):
     check(_lib.load().dsv_verify_attn(ctypes.byref(args), _stream(stream)), "dsv_verify_attn")
 
 
+def verify_attn_noalloc_call(args: AttnArgs, stream=None):
+    """dsv_verify_attn_noalloc: as verify_attn_call, with the split partials in the library's
+    fixed per-GPU scratch array (args.workspace is ignored; no device memory is allocated)."""
+    check(_lib.load().dsv_verify_attn_noalloc(ctypes.byref(args), _stream(stream)),
+          "dsv_verify_attn_noalloc")
+
+
 def pack_verify_attn(args: AttnArgs, block_tokens, out=None, stream=None) -> dict:
     """dsv_pack_verify_attn: the packer fused into the verification launch.  `args` as for
     verify_attn_call (its offsets and slot_cache_loc are ignored); block_tokens [n_bs, W]

@@ -1379,7 +1379,36 @@ struct PackOut {
 };
 }  // namespace dsv
 
-static dsv_status verify_attn_impl(const dsv_attn_args *a, const dsv::PackOut *po, hipStream_t stream) {
+// ---------------------------------------------------------------------------
+// No-allocation variant: the split partials live in a file-scope device array instead of a
+// caller workspace.  Each device holds its own copy; its address is looked up once per device
+// (with that device current) and kept, and only that address is handed to the kernels.  The
+// partials are written before they are read in every call, so nothing is cleared; calls that
+// overlap on one device share the array and race.
+// ---------------------------------------------------------------------------
+namespace dsv {
+constexpr size_t kScratchBytes = DSV_VERIFY_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kScratchDevices = 64;
+static std::atomic<void *> scratch_ptr[kScratchDevices];
+
+// Device address of the current device's scratch array, or null on failure.
+static void *scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return nullptr;
+  void *ptr = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+  scratch_ptr[dev].store(ptr, std::memory_order_release);
+  return ptr;
+}
+}  // namespace dsv
+
+// use_scratch: the split partials go to the current device's scratch array instead of
+// a->workspace (the no-allocation entry point).
+static dsv_status verify_attn_impl(const dsv_attn_args *a, const dsv::PackOut *po, hipStream_t stream,
+                                   bool use_scratch = false) {
   using namespace dsv;
   if (!a || !a->status) return DSV_ERR_INVALID_ARG;
   if (a->dtype != DSV_BF16 && a->dtype != DSV_F32) return DSV_ERR_UNSUPPORTED;
@@ -1424,8 +1453,14 @@ static dsv_status verify_attn_impl(const dsv_attn_args *a, const dsv::PackOut *p
       if (ptr && !aligned(ptr, 16)) return DSV_ERR_INVALID_ARG;
   }
   const Plan pl = make_plan(a);
-  void *const ws = a->workspace;
-  const size_t ws_bytes = a->workspace_bytes;
+  void *ws = a->workspace;
+  size_t ws_bytes = a->workspace_bytes;
+  if (use_scratch) {
+    ws = nullptr;
+    ws_bytes = kScratchBytes;
+    if (pl.ws_o + pl.ws_lse > kScratchBytes) return DSV_ERR_WORKSPACE;
+    if (pl.ws_o + pl.ws_lse > 0 && !(ws = scratch_address())) return DSV_ERR_HIP;
+  }
   if (pl.ws_o + pl.ws_lse > 0 && (!ws || ws_bytes < pl.ws_o + pl.ws_lse || !aligned(ws, 16)))
     return DSV_ERR_WORKSPACE;
 
@@ -1559,6 +1594,10 @@ extern "C" dsv_status dsv_verify_attn(const dsv_attn_args *a, hipStream_t stream
   return verify_attn_impl(a, nullptr, stream);
 }
 
+
+extern "C" dsv_status dsv_verify_attn_noalloc(const dsv_attn_args *a, hipStream_t stream) {
+  return verify_attn_impl(a, nullptr, stream, true);
+}
 
 extern "C" dsv_status dsv_pack_verify_attn(const dsv_attn_args *a, const int32_t *block_tokens,
                                            int32_t *offsets, int32_t *slot_req, int32_t *slot_tok,

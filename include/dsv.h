@@ -259,6 +259,27 @@ size_t dsv_verify_attn_workspace_bytes(const dsv_attn_args *args);
 dsv_status dsv_verify_attn(const dsv_attn_args *args, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* dsv_verify_attn_noalloc -- dsv_verify_attn without a caller workspace     */
+/*                                                                            */
+/* For callers that cannot allocate device memory (code under HIP graph      */
+/* capture, tight serving loops, harnesses that forbid hipMalloc): the same */
+/* computation, kernels and results as dsv_verify_attn(args), with the      */
+/* split-KV partials kept in a fixed device array inside the library        */
+/* (DSV_VERIFY_SCRATCH_BYTES per GPU, held from the library's first use on  */
+/* that GPU until the process ends) instead of args->workspace, which is    */
+/* ignored.  No hipMalloc, hipFree or other allocating call is made.        */
+/* Limit: calls whose dsv_verify_attn_workspace_bytes(args) exceeds          */
+/* DSV_VERIFY_SCRATCH_BYTES return DSV_ERR_WORKSPACE before anything is      */
+/* enqueued (pass a larger kv_chunk, or use dsv_verify_attn).  Calls on one  */
+/* GPU share that GPU's array: calls that may overlap in time on the same   */
+/* GPU (different streams without ordering) race and must not be issued.    */
+/* Other errors: as dsv_verify_attn; DSV_ERR_HIP if the array's device      */
+/* address cannot be obtained.                                               */
+/* ------------------------------------------------------------------------ */
+#define DSV_VERIFY_SCRATCH_BYTES ((size_t)32 << 20)
+dsv_status dsv_verify_attn_noalloc(const dsv_attn_args *args, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* dsv_pack_verify_attn -- the packer fused into the verification launch    */
 /*                                                                            */
 /* DScale Sec. III-C (Flat-buffer packer, Fig. 6) and Sec. III-D (verification */

@@ -93,6 +93,13 @@ def test_host_validation_without_gpu():
     assert lib.dsv_pack_verify_attn(ctypes.byref(b), *outs, None) == 2    # no verification set
     b.n_bs = 2
     assert lib.dsv_pack_verify_attn(ctypes.byref(b), dummy, None, dummy, dummy, dummy, dummy, None) == 1
+    # the no-allocation verification call validates like dsv_verify_attn before it touches
+    # the device (its scratch array is looked up only for a call that needs it)
+    assert lib.dsv_verify_attn_noalloc(None, None) == 1
+    a.d = 96
+    assert lib.dsv_verify_attn_noalloc(ctypes.byref(a), None) == 2
+    a.d = 128
+    assert lib.dsv_verify_attn_noalloc(ctypes.byref(a), None) == 1  # no pools
     # counter-based uniforms: negative length, missing output; an empty stream enqueues nothing
     assert lib.dsv_philox_uniforms(0, 0, 0, 0, -1, ctypes.c_void_p(16), None) == 1
     assert lib.dsv_philox_uniforms(0, 0, 0, 0, 8, None, None) == 1
