@@ -71,9 +71,9 @@ __global__ __launch_bounds__(kAccThreads) void argmax_partial_kernel(
     const int32_t *__restrict__ offsets, int n_bs, uint64_t *__restrict__ keys, int32_t *status) {
   const int64_t bid = blockIdx.x;
   const int row = (int)(bid / n_chunks), c = (int)(bid % n_chunks);
+  // rows at or past the end boundary have no choice to make; the boundary's load goes out
+  // with the first block's loads (a row below m_bs is inside the matrix either way)
   int end = offsets[n_bs];
-  end = end < 0 ? 0 : (end > m_bs ? m_bs : end);
-  if (row >= end) return;
   const int64_t lo = (int64_t)c * chunk;
   const int64_t hi = min(vocab, lo + chunk);
   const float *x = logits + (int64_t)row * vocab;
@@ -114,6 +114,8 @@ __global__ __launch_bounds__(kAccThreads) void argmax_partial_kernel(
     f32x4 fa[kAccLoads], fb[kAccLoads];
     int64_t v0 = lo + 4 * t;
     if (v0 < hi) load(fa, v0);
+    end = end < 0 ? 0 : (end > m_bs ? m_bs : end);
+    if (row >= end) return;
     for (; v0 < hi; v0 += 2 * kAccBlock) {
       if (v0 + kAccBlock < hi) load(fb, v0 + kAccBlock);
       reduce(fa, v0);
@@ -123,6 +125,8 @@ __global__ __launch_bounds__(kAccThreads) void argmax_partial_kernel(
     }
     if (bi >= 0) best = ((uint64_t)ordered_bits(bv) << 32) | (uint32_t)~(uint32_t)bi;
   } else {
+    end = end < 0 ? 0 : (end > m_bs ? m_bs : end);
+    if (row >= end) return;
     for (int64_t v = lo + t; v < hi; v += kAccThreads) {
       float e = x[v];
       nan |= e != e;
@@ -212,7 +216,36 @@ __device__ __forceinline__ uint64_t max_chunk_key(const uint64_t *keys, int64_t 
   return r;
 }
 
-// One wavefront per request.
+// The first four chunk keys (c0, c0 + 4, c0 + 8, c0 + 12) a lane reduces for slot row s; loads
+// are unconditional (indices clamped into the row), so that the caller issues all of them
+// before any is used.
+__device__ __forceinline__ void first_chunk_keys(const uint64_t *keys, int64_t s, int n_chunks, int c0,
+                                                 uint64_t (&v)[4]) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int c = c0 + 4 * u;
+    v[u] = keys[s * n_chunks + (c < n_chunks ? c : n_chunks - 1)];
+  }
+}
+// Largest chunk key of row s from its first four (first_chunk_keys) and the remaining chunks
+// of this lane (c0 + 16, c0 + 20, ...), reduced over the four lanes of the row.
+__device__ __forceinline__ uint64_t row_key(const uint64_t *keys, int64_t s, int n_chunks, int c0,
+                                            const uint64_t (&v)[4]) {
+  uint64_t r = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) r = (c0 + 4 * u < n_chunks && v[u] > r) ? v[u] : r;
+  if (n_chunks > 16) {
+    const uint64_t t = max_chunk_key(keys, s, n_chunks, c0 + 16, 4);
+    r = t > r ? t : r;
+  }
+  uint64_t o = shfl_xor_u64(r, 1);
+  r = o > r ? o : r;
+  o = shfl_xor_u64(r, 2);
+  return o > r ? o : r;
+}
+
+// One wavefront per request.  Two memory round trips before the outputs: the request's fields
+// and the end boundary, then every chunk key and draft token it needs, issued together.
 __global__ __launch_bounds__(kWave) void accept_finalize_kernel(
     int n_bs, int m_bs, int W, const int32_t *__restrict__ slot_tok,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ k,
@@ -224,22 +257,33 @@ __global__ __launch_bounds__(kWave) void accept_finalize_kernel(
   const int i = blockIdx.x;
   const int lane = threadIdx.x;
   if (keys) {
+    const int ki = k[i], off = offsets[i];
     int end = offsets[n_bs];
     end = end < 0 ? 0 : (end > m_bs ? m_bs : end);
-    // every slot's choice: 16 slots per wavefront pass, four lanes per slot (each reducing a
-    // quarter of the slot's chunk keys with its loads in flight together)
+    const bool ok = ki >= 0 && ki <= W && off >= 0 && (int64_t)off + ki <= end;
+    // four lanes per row, 16 rows per wavefront pass: the request's rows off .. off + k_i - 1
+    // and the first pass of the every-slot sweep (slots 16 i ..), with the draft tokens
+    const int jr = lane >> 2, q = lane & 3;
+    const int64_t s_own = ok && jr < ki ? off + jr : 0;
+    const int64_t s_all = (int64_t)i * 16 + jr;
+    uint64_t v_own[4], v_all[4];
+    first_chunk_keys(keys, s_own, n_chunks, q, v_own);
+    first_chunk_keys(keys, s_all < m_bs ? s_all : 0, n_chunks, q, v_all);
+    const int32_t tok_l = slot_tok[ok && lane < ki ? off + lane : 0];
+    // every slot's choice (slot_argmax), 16 slots per pass
     for (int64_t sb = (int64_t)i * 16; sb < m_bs; sb += (int64_t)n_bs * 16) {
-      const int64_t s = sb + (lane >> 2);
-      uint64_t kr = s < end ? max_chunk_key(keys, s, n_chunks, lane & 3, 4) : 0;
-      uint64_t o = shfl_xor_u64(kr, 1);
-      kr = o > kr ? o : kr;
-      o = shfl_xor_u64(kr, 2);
-      kr = o > kr ? o : kr;
-      if ((lane & 3) == 0 && s < m_bs) slot_argmax[s] = s < end ? key_to_index(kr) : -1;
+      const int64_t s = sb + jr;
+      uint64_t kr;
+      if (sb == (int64_t)i * 16) {
+        kr = row_key(keys, s < m_bs ? s : 0, n_chunks, q, v_all);
+      } else {
+        uint64_t v[4];
+        first_chunk_keys(keys, s < m_bs ? s : 0, n_chunks, q, v);
+        kr = row_key(keys, s < m_bs ? s : 0, n_chunks, q, v);
+      }
+      if (q == 0 && s < m_bs) slot_argmax[s] = s < end ? key_to_index(kr) : -1;
     }
 
-    const int ki = k[i], off = offsets[i];
-    const bool ok = ki >= 0 && ki <= W && off >= 0 && (int64_t)off + ki <= end;
     if (!ok) {
       if (lane == 0) {
         status_or(status, DSV_STATUS_BAD_REQUEST);
@@ -256,17 +300,11 @@ __global__ __launch_bounds__(kWave) void accept_finalize_kernel(
       }
       if (out_tokens && lane < W) out_tokens[(int64_t)i * W + lane] = -1;
     } else {
-      // four lanes per row (16 rows per wavefront) reduce the row's chunk keys
-      const int jr = lane >> 2, q = lane & 3;
-      uint64_t kr = jr < ki ? max_chunk_key(keys, off + jr, n_chunks, q, 4) : 0;
-      uint64_t o1 = shfl_xor_u64(kr, 1);
-      kr = o1 > kr ? o1 : kr;
-      o1 = shfl_xor_u64(kr, 2);
-      kr = o1 > kr ? o1 : kr;
+      const uint64_t kr = row_key(keys, s_own, n_chunks, q, v_own);
       // lane j holds the target's choice at slot off + j and the draft token there
       const uint64_t kj = shfl_u64(kr, 4 * (lane & 15));
       const int32_t g = lane < ki ? key_to_index(kj) : -1;
-      const int32_t tok = lane < ki ? slot_tok[off + lane] : -1;
+      const int32_t tok = lane < ki ? tok_l : -1;
       const int32_t g_prev = __shfl(g, lane > 0 ? lane - 1 : 0);
       const bool mismatch = lane >= 1 && lane < ki && tok != g_prev;
       const uint64_t mm = __ballot(mismatch);

@@ -48,6 +48,24 @@ def test_bf16_ragged(d_head, hq, hkv, kv_chunk):
     _run(c, kv_chunk=kv_chunk, tag=f"d{d_head} hq{hq} hkv{hkv} chunk{kv_chunk}")
 
 
+@pytest.mark.parametrize("kv_chunk", [0, 128])
+def test_wide_heads_score_jump_sharp_sentinel(kv_chunk):
+    """head_dim 256 with 12 query heads per KV head (head groups, two waves per head): keys
+    deep in a split whose scores jump far above the split's first tile (a query row's own
+    direction x 30, so the softmax reference must move); the sharp (queries x 8) and
+    leak-detector variants of the same batch run too."""
+    base = small_case(61, hq=12, hkv=1, d=256, k=(16, 7, 3, 1, 12), ctx=(1500, 600, 90, 2000, 33))
+    off = oracle_pack(base)["offsets"]
+    kp = wl.bf16_bits_to_f32(base["k_pool"]).copy()
+    q = wl.bf16_bits_to_f32(base["q"])
+    for i, pos, j, h in ((0, 1330, 5, 2), (3, 1960, 0, 7), (1, 300, 6, 11)):
+        kp[0, int(base["kv_base"][i]) + pos] = q[int(off[i]) + j, h] * np.float32(30.0)
+    jump = dict(base, k_pool=wl.to_bf16_bits(kp), name=base["name"] + "-jump")
+    _run(jump, kv_chunk=kv_chunk, tag=f"score jump chunk{kv_chunk}")
+    _run(wl.sharp_variant(base), kv_chunk=kv_chunk, tag=f"wide sharp chunk{kv_chunk}")
+    _run(wl.sentinel_variant(base), kv_chunk=kv_chunk, tag=f"wide sentinel chunk{kv_chunk}")
+
+
 @pytest.mark.parametrize("d_head", [64, 128, 256])
 def test_fp32_small(d_head):
     c = small_case(31 + d_head, dtype="f32", hq=4, hkv=2, d=d_head, k=(4, 0, 16, 1), ctx=(50, 3, 0, 300))
