@@ -69,7 +69,8 @@ struct AttnParams {
   void *out;
   float *lse;
   int chunk, n_splits;
-  float *ws_o, *ws_lse;  // [n_splits][m_bs][hq][D], [n_splits][m_bs][hq]
+  uint16_t *ws_o;       // [n_splits][m_bs][hq][D] bf16 split outputs
+  float *ws_lse;        // [n_splits][m_bs][hq]
   // prefill set
   int n_pf, pf_blocks, pf_q_rows, pf_max_len;
   const int32_t *pf_q_start, *pf_q_len, *pf_ctx;
@@ -359,8 +360,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     n_splits_i = verify_splits(p, n_vis);
     if (ki == 0 || split >= n_splits_i) return;
     if (MAP) kvi = p.kv_index + (int64_t)i * p.kv_index_stride;
-    r_lo = split * p.chunk;
-    r_hi = split == n_splits_i - 1 ? n_vis : r_lo + p.chunk;
+    // the candidate block costs about one tile: the last split hands one committed tile to
+    // the split before it
+    const int shift = (n_splits_i >= 2 && n_vis - (n_splits_i - 1) * p.chunk >= 2 * kTileKV + ki) ? kTileKV : 0;
+    r_lo = split * p.chunk + (split == n_splits_i - 1 ? shift : 0);
+    r_hi = split == n_splits_i - 1 ? n_vis : r_lo + p.chunk + (split == n_splits_i - 2 ? shift : 0);
     row0 = 0;
     nrows = ki;
     q_row0 = off;
@@ -924,13 +928,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     float *lse = PF ? p.pf_lse : p.lse;
     if (lse && lg == 0 && dpart == 0) gstore(lse + orow * p.hq + h, lse_v);
   } else {
-    // partials are read once, by the merge kernel: streaming (non-temporal) stores
-    float *o = p.ws_o + (((int64_t)split * p.m_bs + orow) * p.hq + h) * D;
+    // partials are read once, by the merge kernel: streaming (non-temporal) stores, rounded to
+    // bf16 like the output itself (half the bytes of the write-back and of the merge's reads;
+    // the merge weights and sums them in fp32)
+    uint16_t *o = p.ws_o + (((int64_t)split * p.m_bs + orow) * p.hq + h) * D;
 #pragma unroll
     for (int db = 0; db < DBW; ++db) {
       const int d = 16 * (dpart * DBW + db) + 4 * lg;
-      gstore_stream(o + d, f32x4{acc_o[db][0] * inv_l, acc_o[db][1] * inv_l, acc_o[db][2] * inv_l,
-                                 acc_o[db][3] * inv_l});
+      gstore_stream(o + d, u32x2{cvt_pk_bf16(acc_o[db][0] * inv_l, acc_o[db][1] * inv_l),
+                                 cvt_pk_bf16(acc_o[db][2] * inv_l, acc_o[db][3] * inv_l)});
     }
     if (lg == 0 && dpart == 0)
       gstore_stream(p.ws_lse + ((int64_t)split * p.m_bs + orow) * p.hq + h, lse_v);
@@ -938,7 +944,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
 }
 
 // ---------------------------------------------------------------------------
-// Split-KV merge: out = sum_s e^{lse_s - M} o_s / sum_s e^{lse_s - M}, lse = M + ln(sum),
+// Split-KV merge (split outputs o_s stored in bf16, weights and sums in fp32):
+// out = sum_s e^{lse_s - M} o_s / sum_s e^{lse_s - M}, lse = M + ln(sum),
 // splits taken in increasing order with a running maximum (deterministic).  Half a wavefront (32 lanes x 4 floats)
 // per (slot, query head) row of D = 128 (D/4 lanes in general), all of a row's split loads
 // issued before they are consumed.  Requests whose KV range fits one split were written
@@ -974,7 +981,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
   // time are all issued before any is combined
   float M = -INFINITY, den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
-  const f32x4 *src = reinterpret_cast<const f32x4 *>(p.ws_o + rh * D) + l4;
+  const u32x2 *src = reinterpret_cast<const u32x2 *>(p.ws_o + rh * D) + l4;
   const int64_t step4 = plane * D / 4;
   constexpr int kBatch = 8;
   for (int s0 = 0; s0 < S; s0 += kBatch) {
@@ -984,7 +991,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p) {
     for (int u = 0; u < kBatch; ++u) {
       const int s = s0 + u;
       ls[u] = s < S ? gload<float>(p.ws_lse + s * plane + rh) : -INFINITY;
-      o[u] = s < S ? gload<f32x4>(src + s * step4) : f32x4{0.f, 0.f, 0.f, 0.f};
+      const u32x2 b = s < S ? gload<u32x2>(src + s * step4) : u32x2{0u, 0u};
+      o[u] = f32x4{bf16_bits_to_f32(b[0] & 0xffffu), bf16_bits_to_f32(b[0] >> 16),
+                   bf16_bits_to_f32(b[1] & 0xffffu), bf16_bits_to_f32(b[1] >> 16)};
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
@@ -1263,7 +1272,7 @@ static Plan make_plan(const dsv_attn_args *a) {
   pl.n_splits = (int)(rows / chunk);
   if (pl.n_splits < 1) pl.n_splits = 1;
   if (pl.n_splits > 1) {
-    pl.ws_o = align256((size_t)pl.n_splits * a->m_bs * a->hq * a->d * sizeof(float));
+    pl.ws_o = align256((size_t)pl.n_splits * a->m_bs * a->hq * a->d * sizeof(uint16_t));
     pl.ws_lse = align256((size_t)pl.n_splits * a->m_bs * a->hq * sizeof(float));
   }
   return pl;
@@ -1500,7 +1509,7 @@ static dsv_status verify_attn_impl(const dsv_attn_args *a, const dsv::PackOut *p
   p.lse = a->lse;
   p.chunk = pl.chunk;
   p.n_splits = pl.n_splits;
-  p.ws_o = pl.ws_o ? static_cast<float *>(ws) : nullptr;
+  p.ws_o = pl.ws_o ? static_cast<uint16_t *>(ws) : nullptr;
   p.ws_lse = pl.ws_o ? reinterpret_cast<float *>(static_cast<char *>(ws) + pl.ws_o) : nullptr;
   p.n_pf = a->n_pf;
   p.pf_max_len = a->pf_max_len;
