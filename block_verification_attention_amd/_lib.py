@@ -5,7 +5,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdsv.so")
+# DSV_LIBRARY: another build of the library to load instead (for example a sanitizer build of
+# its host code); by default the in-tree libdsv.so
+LIB_PATH = os.environ.get("DSV_LIBRARY") or os.path.join(_HERE, "libdsv.so")
 
 DSV_BF16 = 0
 DSV_F32 = 1

@@ -75,7 +75,8 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        lib = ctypes.CDLL(build())
+        # DSV_ORACLE_LIBRARY: another build of the same C source (the sanitizer runs use one)
+        lib = ctypes.CDLL(os.environ.get("DSV_ORACLE_LIBRARY") or build())
         P = ctypes.c_void_p
         i32, i64, dbl = ctypes.c_int, ctypes.c_int64, ctypes.c_double
         lib.oracle_pack.argtypes = [i32, i32, i32] + [P] * 9
