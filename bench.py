@@ -306,6 +306,72 @@ def time_prefill(dev, iters: int = 20):
             "status": int(st.item())}
 
 
+def time_mixed(dev, iters: int = 10):
+    """The mixed launch (60 verification requests with ragged prefixes in 480 slots at
+    contexts U[8192, 32768], plus 4 fresh prefill requests of 4096 causal rows; 32 / 8 heads,
+    head_dim 128, bf16) as ONE dsv_verify_attn call, next to its two halves called alone on
+    the same inputs: median of `iters` calls each, HIP events around each call.  K/V pool
+    drawn on the device, N(0,1) * 0.5 (about 5 GB, far above the Infinity Cache)."""
+    import numpy as np
+    import torch
+    import block_verification_attention_amd as dsv
+    import workloads as wl
+    c = wl.config5(draw=False)
+    hq, hkv, d, W = c["hq"], c["hkv"], c["d"], c["W"]
+    pf = c["prefill"]
+    pf_rows = int(pf["q_len"].sum())
+    g = torch.Generator(device=dev)
+    g.manual_seed(5201)
+    rnd = lambda shape: (torch.randn(shape, generator=g, device=dev) * 0.5).to(torch.bfloat16)  # noqa: E731
+    kp, vp = rnd((hkv, c["pool_rows"], d)), rnd((hkv, c["pool_rows"], d))
+    q, kn, vn, pq = rnd((c["m_bs"], hq, d)), rnd((c["m_bs"], hkv, d)), rnd((c["m_bs"], hkv, d)), rnd((pf_rows, hq, d))
+    td = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    kd, cd, bd, tok = td(c["k"]), td(c["ctx_len"]), td(c["kv_base"]), td(c["block_tokens"])
+    st = dsv.new_status(dev)
+    packed = dsv.pack_slots(kd, cd, bd, tok, c["m_bs"], st)
+    prefill = dsv.Prefill(q_start=td(pf["q_start"]), q_len=td(pf["q_len"]), ctx_len=td(pf["ctx_len"]),
+                          kv_base=td(pf["kv_base"]), q=pq, out=torch.empty_like(pq), max_len=pf["max_len"],
+                          lse=torch.empty((pf_rows, hq), dtype=torch.float32, device=dev))
+    out = torch.empty_like(q)
+    lse = torch.empty((c["m_bs"], hq), dtype=torch.float32, device=dev)
+    max_ctx = int(c["ctx_len"].max())
+
+    def make(verify, pre):
+        if verify:
+            a = dsv.attn_args(q, kp, vp, packed["offsets"], kd, cd, bd, W=W, max_ctx=max_ctx, out=out, status=st,
+                              lse=lse, k_new=kn, v_new=vn, slot_cache_loc=packed["slot_cache_loc"],
+                              prefill=prefill if pre else None)
+        else:
+            a = dsv.attn_args(None, kp, vp, None, None, None, None, W=W, max_ctx=0, out=None, status=st,
+                              prefill=prefill)
+        return a
+
+    res = {}
+    for name, a in (("mixed_us", make(True, True)), ("verify_only_us", make(True, False)),
+                    ("prefill_only_us", make(False, True))):
+        ws = torch.empty(max(dsv.verify_attn_workspace_bytes(a), 256), dtype=torch.uint8, device=dev)
+        a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+        for _ in range(2):
+            dsv.verify_attn_call(a)
+        evs = []
+        for _ in range(iters):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            dsv.verify_attn_call(a)
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        res[name] = float(np.median([x.elapsed_time(y) for x, y in evs])) * 1e3
+        del ws
+    res["mixed_over_sum_of_halves"] = res["mixed_us"] / (res["verify_only_us"] + res["prefill_only_us"])
+    res["slots"] = int(c["k"].sum())
+    res["prefill_rows"] = pf_rows
+    res["status"] = int(st.item())
+    del kp, vp
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_other_verify(dev, ev, iters: int = 20):
     """Verification attention on the two other verification shapes of the configuration set,
     with their seeded prefix lengths and contexts and seeded N(0,1) * 0.5 device-made K/V:
@@ -433,6 +499,98 @@ def _cpu_baseline(case, n_req_sample, min_seconds, max_reps):
     }
 
 
+def cpu_configs(dev):
+    """The oracle on every configuration of the workload set, on one host thread and on every
+    host thread: pack + fp64 verification attention (+ greedy accept over the target logits,
+    or the draft top-1/top-2 margin), computed in full for configs 1-4; for config 5 all 480
+    verification slots plus 512 prefill rows of each of its 4 requests (the first 64, the last
+    64 and 384 seeded ones between them).  Wall time is the best of 3 passes, or one pass when
+    it exceeds 10 s.  Config 5's pool (~5 GB) is drawn on the device and copied to the host."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads as wl
+
+    def best_of(fn):
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+            if ts[-1] > 10.0:
+                break
+        return min(ts), len(ts)
+
+    def verify_pass(c):
+        p = oracle.pack(c["k"], c["ctx_len"], c["kv_base"], c["block_tokens"], c["W"], c["m_bs"])
+        oracle.verify_attn(c["q"], c["k_pool"], c["v_pool"], p["offsets"], c["k"], c["ctx_len"], c["kv_base"],
+                           c["k_new"], c["v_new"])
+        return p
+
+    cases = {}
+    def verify_accept(*steps):
+        for c in steps:
+            p = verify_pass(c)
+            oracle.accept(c["logits"], p["slot_tok"], p["offsets"], c["k"], c["W"])
+
+    c1 = wl.config1()
+    cases["1"] = (int(c1["k"].sum()), lambda: verify_accept(c1))
+    s1, s2 = wl.config2()
+    cases["2"] = (int(s1["k"].sum() + s2["k"].sum()), lambda: verify_accept(s1, s2))
+    c3 = wl.config3()
+    cases["3"] = (int(c3["k"].sum()), lambda: verify_accept(c3))
+    c4 = wl.config4()
+
+    def cfg4():
+        verify_pass(c4)
+        oracle.top2_margin(c4["draft_logits"])
+    cases["4"] = (int(c4["k"].sum()), cfg4)
+    # config 5: pool, queries and candidates drawn on the device, then copied to the host
+    c5 = wl.config5(draw=False)
+    g = torch.Generator(device=dev)
+    g.manual_seed(5301)
+    bits = lambda t: t.cpu().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+    rnd = lambda shape: bits((torch.randn(shape, generator=g, device=dev) * 0.5).to(torch.bfloat16))  # noqa: E731
+    hkv, hq, d = c5["hkv"], c5["hq"], c5["d"]
+    pf = c5["prefill"]
+    pf_rows = int(pf["q_len"].sum())
+    c5 = dict(c5, k_pool=rnd((hkv, c5["pool_rows"], d)), v_pool=rnd((hkv, c5["pool_rows"], d)),
+              q=rnd((c5["m_bs"], hq, d)), k_new=rnd((c5["m_bs"], hkv, d)), v_new=rnd((c5["m_bs"], hkv, d)))
+    pq = rnd((pf_rows, hq, d))
+    sel = np.random.default_rng(5110)
+    sel_req, sel_j = [], []
+    for r in range(pf["n_pf"]):
+        ql = int(pf["q_len"][r])
+        js = sorted(set(range(64)) | set(range(ql - 64, ql)) |
+                    set(sel.choice(np.arange(64, ql - 64), 384, replace=False).tolist()))
+        sel_req += [r] * len(js)
+        sel_j += js
+
+    def cfg5():
+        verify_pass(c5)
+        oracle.prefill_attn(pq, c5["k_pool"], c5["v_pool"], pf["q_start"], pf["q_len"], pf["ctx_len"],
+                            pf["kv_base"], sel_req, sel_j)
+    cases["5"] = (int(c5["k"].sum()), cfg5)
+
+    nproc = os.cpu_count() or 1
+    default_threads = oracle.threads()
+    out = {}
+    try:
+        for name, (slots, fn) in cases.items():
+            row = {"slots": slots}
+            for th in (1, default_threads):
+                oracle.set_threads(th)
+                sec, passes = best_of(fn)
+                row[f"threads_{th}"] = {"seconds": sec, "slots_per_s": slots / sec, "passes": passes}
+                print(f"cpu config {name} threads {th}: {sec:.3f} s", file=sys.stderr, flush=True)
+            out[name] = row
+    finally:
+        oracle.set_threads(default_threads)
+    out["5"]["sample"] = "all 480 verification slots + 512 prefill rows per request (first 64, last 64, 384 seeded)"
+    return {"cpu_configs": out, "cpu_model": cpu_model(), "nproc": nproc, "oracle_threads": default_threads}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -441,6 +599,8 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="KV/logits copies rotated per step")
     ap.add_argument("--kv-chunk", type=int, default=0)
     ap.add_argument("--cpu-sample", type=int, default=8, help="requests in the oracle sample (0 = skip)")
+    ap.add_argument("--cpu-configs", action="store_true",
+                    help="only time the CPU oracle on every configuration (1 and all host threads)")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="launch each step's calls directly instead of replaying a captured HIP graph")
     args = ap.parse_args()
@@ -457,6 +617,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.cpu_configs:
+        print(json.dumps(cpu_configs(dev)))
+        return
     dsv.load_library()
     c = wl.config3()
 
@@ -677,6 +840,7 @@ def main():
     res["features"] = time_features(dev)
     res["prefill"] = time_prefill(dev)
     res["other_verify"] = time_other_verify(dev, ev)
+    res["mixed_launch"] = time_mixed(dev)
     if args.cpu_sample > 0:
         res["cpu_baseline"] = cpu_baseline(c, args.cpu_sample)
         # the same oracle on one thread, over one request (16 slots)
