@@ -42,9 +42,9 @@ PROFILED_KERNEL = "attn_bf16_kernel<128, 8, false, 64, 2, false, 1>"
 # WRITE_SIZE runs (profiles/attn_verify_cfg3_hbm_traffic.md, calibrated there against the
 # streaming-read probe and a pool copy), valid for the kernel source with this SHA-256 only.
 COUNTED_SOURCE = ("block_verification_attention_amd/csrc/dsv_attn.hip",
-                  "7854fabe0c01e8044aa74fadbab0f846152e6fa199938ad12799bd22f02db453")
-COUNTED_READ_BYTES = 270_334_286
-COUNTED_WRITE_BYTES = 10_978_304
+                  "a0b6f4c79f27373deb8153afd917ac2afe075f11b5c258e9d276e44de0c02e6d")
+COUNTED_READ_BYTES = 270_437_680
+COUNTED_WRITE_BYTES = 6_161_787
 
 
 def counted_traffic():
