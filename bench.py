@@ -37,7 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-PROFILED_KERNEL = "attn_bf16_kernel<128, 8, false, 64, 2, false, 1>"
+PROFILED_KERNEL = "attn_bf16_kernel<128, 8, false, 64, 2, false>"
 # HBM bytes per launch of that kernel on this workload, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE runs (profiles/attn_verify_cfg3_hbm_traffic.md, calibrated there against the
 # streaming-read probe and a pool copy), valid for the kernel source with this SHA-256 only.
@@ -301,7 +301,7 @@ def time_prefill(dev, iters: int = 20):
     flop = 4.0 * hq * d * n_req * q_len * (q_len + 1) / 2
     tflops = flop / (us * 1e-6) / 1e12
     return {"workload": "prefill, 4 x 4096 causal rows, 32/8 heads, head_dim 128, bf16",
-            "kernel": "attn_bf16_kernel<128, 8, true, 64, 1, false, 1>", "us": us, "flop": flop,
+            "kernel": "attn_bf16_kernel<128, 8, true, 64, 1, false>", "us": us, "flop": flop,
             "TFLOPs": tflops, "peak_TFLOPs": 2500.0, "frac": tflops / 2500.0,
             "status": int(st.item())}
 

@@ -37,19 +37,18 @@ def hipcc() -> str:
     return "hipcc"
 
 
-# attn_bf16_kernel<D, NW, PF, TILE, HV, MAP, DS>
-_ATTN_KERNEL = re.compile(r"attn_bf16_kernelILi(\d+)ELi(\d+)ELb([01])ELi(\d+)ELi(\d+)ELb([01])ELi(\d+)E")
+# attn_bf16_kernel<D, NW, PF, TILE, HV, MAP>
+_ATTN_KERNEL = re.compile(r"attn_bf16_kernelILi(\d+)ELi(\d+)ELb([01])ELi(\d+)ELi(\d+)ELb([01])E")
 
 
 def attn_kernel_resources(remarks: str) -> dict:
-    """Per attention-kernel instantiation (D, waves, prefill, KV halves, cache map, waves per head): VGPRs, AGPRs, scratch bytes per
-    lane and occupancy (waves per SIMD), parsed from the compiler's resource-usage remarks."""
+    """Per attention-kernel instantiation (D, waves, prefill, KV halves, cache map): VGPRs, AGPRs, scratch
+    bytes per lane and occupancy (waves per SIMD), parsed from the compiler's resource-usage remarks."""
     res, cur = {}, None
     for line in remarks.splitlines():
         if "Function Name:" in line:
             m = _ATTN_KERNEL.search(line)
-            cur = (int(m.group(1)), int(m.group(2)), m.group(3) == "1", int(m.group(5)), m.group(6) == "1",
-                   int(m.group(7))) if m else None
+            cur = (int(m.group(1)), int(m.group(2)), m.group(3) == "1", int(m.group(5)), m.group(6) == "1") if m else None
             if cur:
                 res[cur] = {}
         elif cur is not None:
@@ -86,9 +85,8 @@ def build(verbose: bool = False) -> str:
             if not res:
                 raise RuntimeError("no attention kernel found in the resource report")
             if verbose:
-                for (d, nw, pf, hv, mp, ds), r in sorted(res.items()):
-                    print(f"attn_bf16_kernel D={d} waves={nw} prefill={pf} halves={hv} map={mp} "
-                          f"waves_per_head={ds}: {r}")
+                for (d, nw, pf, hv, mp), r in sorted(res.items()):
+                    print(f"attn_bf16_kernel D={d} waves={nw} prefill={pf} halves={hv} map={mp}: {r}")
             lines = [l for l in lines if "remark:" not in l and "kernel-resource-usage" not in l]
         msg = "\n".join(lines)
         if msg.strip() and verbose:

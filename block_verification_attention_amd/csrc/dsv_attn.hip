@@ -207,20 +207,17 @@ constexpr float kRescaleSlack = 8.0f;
 // tile per query head, split KV).  PF = true: prefill (NW = 8 waves along the query rows of
 // one head).  KV tiles of TILE rows stream through an NSTAGE-deep LDS ring.
 // ---------------------------------------------------------------------------
-template <int D, int NW>
+template <int D, int NW, bool PF>
 constexpr int waves_per_eu_hint() {
-  // small workgroups get the whole register file; 3..8 waves are asked to fit 2 waves/SIMD,
-  // and at head_dim 128 and 256 exactly 2 (a third wave per SIMD cannot host another
-  // workgroup of this size, and tighter register budgets cost the tile loop its loads in
-  // flight); head_dim-64 kernels may run more per SIMD
-  return (NW <= 2 || (D == 256 && NW <= 4)) ? 1 : (NW <= 8 ? 2 : 1);
+  // small workgroups and the 4-wave head_dim-256 prefill get the whole register file; 3..8
+  // waves are asked to fit 2 waves/SIMD, and at head_dim 128 and 256 exactly 2 (a third wave
+  // per SIMD cannot host another workgroup of this size, and tighter register budgets cost
+  // the tile loop its loads in flight); head_dim-64 kernels may run more per SIMD
+  return (NW <= 2 || (D == 256 && NW <= 4 && PF)) ? 1 : (NW <= 8 ? 2 : 1);
 }
 
-// DS (verification, one KV half): waves per query head, each accumulating D / DS of the
-// output columns (both compute the head's scores), so that a wave holds D / (4 DS) output
-// registers per lane.
-template <int D, int NW, bool PF, int TILE, int HV, bool MAP, int DS = 1>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_per_eu_hint<D, NW>(), waves_per_eu_hint<D, NW>() == 2 && D >= 128 ? 2 : 10))) void attn_bf16_kernel(AttnParams p) {
+template <int D, int NW, bool PF, int TILE, int HV, bool MAP>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_per_eu_hint<D, NW, PF>(), waves_per_eu_hint<D, NW, PF>() == 2 && D >= 128 ? 2 : 10))) void attn_bf16_kernel(AttnParams p) {
   constexpr int RPC = 1024 / (2 * D);        // rows per 1 KB wave load
   constexpr int NCK = TILE / RPC;            // wave loads per tensor per tile
   constexpr int NP = 2 * NCK * HV;           // wave loads per stage (HV tiles of K and V)
@@ -234,8 +231,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
   static_assert(NW % HV == 0, "wave halves");
   constexpr int DB = D / 16;
   constexpr int KS = D / 32;
-  static_assert(DS == 1 || (!PF && HV == 1 && NW % DS == 0), "output split: verification, one half");
-  constexpr int DBW = DB / DS;  // output column blocks of this wave
   static_assert(TILE % 32 == 0 && TILE % RPC == 0, "tile shape");
 
   extern __shared__ __align__(16) uint16_t lds[];
@@ -247,8 +242,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
   // KV half of this wave (HV = 2: waves [0, NWH) consume the even tiles of each stage pair,
   // waves [NWH, NW) the odd ones, for the same query heads) and its head within the group
   const int half = HV == 1 ? 0 : w / NWH;
-  const int wh = (HV == 1 ? w : w - half * NWH) / DS;  // head within the workgroup's heads
-  const int dpart = DS == 1 ? 0 : w % DS;             // output columns [D dpart / DS, +D / DS)
+  const int wh = HV == 1 ? w : w - half * NWH;  // head within the workgroup's heads
 
   // ---- work unit ----
   int g, h, c, r_lo, r_hi, row0, nrows, split = 0, n_splits_i = 1, off = 0, hg = 0;
@@ -574,18 +568,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     koff[ks] = lds_base + half * SUB_BYTES + lq * (2 * D) + k_slot<D>(lq, 4 * ks + lg) * 16;
   // V (transposing reads): row R + lq/4 with R = 32kk + 16half + 4lg, 8 bytes at column
   // 16db + 4(lq%4); the row term 32kk + 16half does not change the swizzle
-  uint32_t voffs[DBW];
+  uint32_t voffs[DB];
 #pragma unroll
-  for (int dbw = 0; dbw < DBW; ++dbw) {
-    const int db = dpart * DBW + dbw;
+  for (int db = 0; db < DB; ++db) {
     const int row = 4 * lg + (lq >> 2);
-    voffs[dbw] = lds_base + half * SUB_BYTES + TILE * D * 2 + row * (2 * D) +
+    voffs[db] = lds_base + half * SUB_BYTES + TILE * D * 2 + row * (2 * D) +
                  v_slot<D>(row, 2 * db + ((lq & 3) >> 1)) * 16 + 8 * (lq & 1);
   }
 
-  f32x4 acc_o[DBW];
+  f32x4 acc_o[DB];
 #pragma unroll
-  for (int db = 0; db < DBW; ++db) acc_o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < DB; ++db) acc_o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_ref = -INFINITY, l_run = 0.f;  // reference max (log2 units) and row-sum partial
 
   const int n_tiles = (t_hi - r_lo + HV * TILE - 1) / (HV * TILE);  // stages of HV tiles
@@ -640,7 +633,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
       m_ref = m_new;
       l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < DBW; ++db) acc_o[db] *= alpha;
+      for (int db = 0; db < DB; ++db) acc_o[db] *= alpha;
     }
     const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
     // P (bf16) is the B operand of O^T = V^T P^T; the row sum accumulates the fp32 values
@@ -661,7 +654,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
       const bf16x8 b = __builtin_bit_cast(
           bf16x8, make_uint4(pb[2 * kk][0], pb[2 * kk][1], pb[2 * kk + 1][0], pb[2 * kk + 1][1]));
 #pragma unroll
-      for (int db = 0; db < DBW; ++db) {
+      for (int db = 0; db < DB; ++db) {
         // transposing reads: lane j of each 16-lane group receives V[R + t][16db + j], t < 4,
         // from the 8-byte chunks that lanes j/4 + 4t point at (rows R + lq/4, columns
         // 16db + 4(lq%4)); R = 32kk + 16half + 4lg.
@@ -889,20 +882,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     auto at = [&](int k) __attribute__((always_inline)) { return (k * NWH + wh) * 64 + lane; };
     if (half == 1) {
 #pragma unroll
-      for (int db = 0; db < DBW; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int e = 0; e < 4; ++e) xs[at(4 * db + e)] = acc_o[db][e];
-      xs[at(4 * DBW)] = m_ref;
-      xs[at(4 * DBW + 1)] = l_run;
+      xs[at(4 * DB)] = m_ref;
+      xs[at(4 * DB + 1)] = l_run;
     }
     __syncthreads();
     if (half == 1) return;
-    const float m1 = xs[at(4 * DBW)], l1 = xs[at(4 * DBW + 1)];
+    const float m1 = xs[at(4 * DB)], l1 = xs[at(4 * DB + 1)];
     const float m_new = fmaxf(m_ref, m1);
     const float a0 = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
     const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m_new);
 #pragma unroll
-    for (int db = 0; db < DBW; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc_o[db][e] = acc_o[db][e] * a0 + xs[at(4 * db + e)] * a1;
     l_run = l_run * a0 + l1 * a1;
@@ -920,25 +913,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
   if (PF || n_splits_i == 1) {
     uint16_t *o = static_cast<uint16_t *>(PF ? p.pf_out : p.out) + (orow * p.hq + h) * (int64_t)D;
 #pragma unroll
-    for (int db = 0; db < DBW; ++db) {
-      const int d = 16 * (dpart * DBW + db) + 4 * lg;
+    for (int db = 0; db < DB; ++db) {
+      const int d = 16 * db + 4 * lg;
       gstore(o + d, u32x2{cvt_pk_bf16(acc_o[db][0] * inv_l, acc_o[db][1] * inv_l),
                           cvt_pk_bf16(acc_o[db][2] * inv_l, acc_o[db][3] * inv_l)});
     }
     float *lse = PF ? p.pf_lse : p.lse;
-    if (lse && lg == 0 && dpart == 0) gstore(lse + orow * p.hq + h, lse_v);
+    if (lse && lg == 0) gstore(lse + orow * p.hq + h, lse_v);
   } else {
     // partials are read once, by the merge kernel: streaming (non-temporal) stores, rounded to
     // bf16 like the output itself (half the bytes of the write-back and of the merge's reads;
     // the merge weights and sums them in fp32)
     uint16_t *o = p.ws_o + (((int64_t)split * p.m_bs + orow) * p.hq + h) * D;
 #pragma unroll
-    for (int db = 0; db < DBW; ++db) {
-      const int d = 16 * (dpart * DBW + db) + 4 * lg;
+    for (int db = 0; db < DB; ++db) {
+      const int d = 16 * db + 4 * lg;
       gstore_stream(o + d, u32x2{cvt_pk_bf16(acc_o[db][0] * inv_l, acc_o[db][1] * inv_l),
                                  cvt_pk_bf16(acc_o[db][2] * inv_l, acc_o[db][3] * inv_l)});
     }
-    if (lg == 0 && dpart == 0)
+    if (lg == 0)
       gstore_stream(p.ws_lse + ((int64_t)split * p.m_bs + orow) * p.hq + h, lse_v);
   }
 }
@@ -1186,18 +1179,14 @@ static int verify_halves(int G) { return G <= 4 ? 2 : 1; }
 // Longest automatic split when the units alone fill the GPU (a multiple of kTileKV).
 constexpr int64_t kBalanceRows = 4096;
 
-// Query heads per workgroup for head_dim 256 (two waves per head): at most this many.
-#ifndef DSV_WIDE_HEADS_PER_WG
-#define DSV_WIDE_HEADS_PER_WG 4
-#endif
-constexpr int kWideHeadsPerWg = DSV_WIDE_HEADS_PER_WG;
+// Query heads per workgroup for head_dim 256: at most this many.
+constexpr int kWideHeadsPerWg = 4;
 
 // Query heads per verification workgroup.  For head_dim 256 a head's output accumulators
-// (64 registers per lane) plus its query fragment do not leave room for the rest of a wave's
-// state at two or three waves per SIMD, so each head gets two waves that split the output
-// columns (verify_waves_per_head), and a KV head's query heads are spread over
-// HG = ceil(G / GW) workgroups of 2 GW waves, which each read the KV head's rows, with at
-// most kWideHeadsPerWg heads each.  At head_dim 128 more than 8 one-head waves per
+// take 64 registers per lane, so a KV head's query heads are spread over HG = ceil(G / GW)
+// workgroups of 4 one-head waves (two per CU, 2 waves per SIMD, 64 KB of LDS each), which
+// each read the KV head's rows, with at most kWideHeadsPerWg heads each.  At head_dim 128
+// more than 8 one-head waves per
 // workgroup would run at 3-4 waves per SIMD and spill, so larger groups are split the same
 // way into workgroups of at most 8 heads.  The groups are as even as possible (the last one
 // may hold fewer heads: its spare waves only move tile loads).
@@ -1215,9 +1204,6 @@ static int verify_head_groups(int D, int G) {
   const int gw = verify_heads_per_wg(D, G);
   return (G + gw - 1) / gw;
 }
-
-// Waves per query head in the verification kernel (output columns split between them).
-static int verify_waves_per_head(int D) { return D >= 256 ? 2 : 1; }
 
 // Compute units of the current device, read once per device (256 on a whole MI355X; fewer
 // on a partitioned one).  Without a usable device (a host-only workspace query) the plan
@@ -1252,11 +1238,10 @@ static Plan make_plan(const dsv_attn_args *a) {
     const int GW = verify_heads_per_wg(a->d, G);
     const int64_t units = (int64_t)a->n_bs * a->hkv * verify_head_groups(a->d, G);
     // wave groups in flight: two per SIMD (512 groups of G waves, or 256 two-half ones); the
-    // wide-head workgroups (2 GW waves, one per CU at a time) aim at four rounds, whose
-    // shorter splits balance requests of different lengths (32 requests at 4k-8k with 12
-    // heads per KV head: 270 us at two splits, 247-264 us at 512-1344-row splits)
+    // wide-head workgroups (4 waves, two per CU at a time) aim at two rounds, whose shorter
+    // splits balance requests of different lengths
     const int64_t cus = device_cus();
-    const int64_t wgs = verify_waves_per_head(a->d) == 2 ? 4 * cus : 2 * cus / verify_halves(GW);
+    const int64_t wgs = a->d >= 256 ? 4 * cus : 2 * cus / verify_halves(GW);
     int64_t target = (wgs + units - 1) / units;
     if (target < 1) target = 1;
     if (target > 64) target = 64;
@@ -1286,15 +1271,15 @@ template <> struct TileCfg<256> { static constexpr int TILE = 32; };
 
 // ev0 / ev1 (optional) are attached to the launch itself: their timestamps are the kernel's
 // start and end.
-template <int D, int NW, bool PF, int HV = 1, bool MAP = false, int DS = 1>
+template <int D, int NW, bool PF, int HV = 1, bool MAP = false>
 static bool launch_attn_k(const AttnParams &p, int grid, hipStream_t s, hipEvent_t ev0 = nullptr,
                           hipEvent_t ev1 = nullptr) {
   // the two-waves-per-head verification kernel takes 64-row tiles when a tile's wave loads
   // split evenly over its waves (fewer, longer stages; otherwise the uneven piece pattern
   // spills)
-  constexpr int TILE = (DS > 1 && (64 / (1024 / (2 * D))) % NW == 0) ? 64 : TileCfg<D>::TILE;
+  constexpr int TILE = TileCfg<D>::TILE;
   constexpr size_t shm = (size_t)(PF ? 3 : 2) * HV * 2 * TILE * D * sizeof(uint16_t);
-  auto kern = attn_bf16_kernel<D, NW, PF, TILE, HV, MAP, DS>;
+  auto kern = attn_bf16_kernel<D, NW, PF, TILE, HV, MAP>;
   // once per kernel (idempotent), so that a captured call contains launches only
   static bool lds_limit_set = false;
   if (!lds_limit_set) {
@@ -1312,25 +1297,24 @@ static bool launch_attn_k(const AttnParams &p, int grid, hipStream_t s, hipEvent
 
 // The cache-map variant is a separate instantiation, so that the contiguous kernel carries
 // none of its registers.
-template <int D, int NW, bool PF, int HV = 1, int DS = 1>
+template <int D, int NW, bool PF, int HV = 1>
 static bool launch_attn(const AttnParams &p, int grid, hipStream_t s, hipEvent_t ev0 = nullptr,
                         hipEvent_t ev1 = nullptr) {
   if constexpr (!PF) {
-    if (p.kv_index) return launch_attn_k<D, NW, PF, HV, true, DS>(p, grid, s, ev0, ev1);
+    if (p.kv_index) return launch_attn_k<D, NW, PF, HV, true>(p, grid, s, ev0, ev1);
   }
-  return launch_attn_k<D, NW, PF, HV, false, DS>(p, grid, s, ev0, ev1);
+  return launch_attn_k<D, NW, PF, HV, false>(p, grid, s, ev0, ev1);
 }
 
 template <int D>
 static int launch_verify_g(const AttnParams &p, int grid, hipStream_t s, hipEvent_t e0,
                            hipEvent_t e1) {
   if constexpr (D >= 256) {
-    // wide heads: two waves per head, each with half of the output columns, one KV half
-    static_assert(kWideHeadsPerWg >= 1 && kWideHeadsPerWg <= 4, "wide-head workgroups");
-    // (groups of one or two heads are refused by the host checks)
+    // wide heads: groups of 3 heads (G = 3, 5, 6, 9) run padded to 4 waves; groups of one
+    // or two heads are refused by the host checks
     switch (p.GW) {
-      case 3: return launch_attn<D, 6, false, 1, 2>(p, grid, s, e0, e1);
-      case 4: return launch_attn<D, 8, false, 1, 2>(p, grid, s, e0, e1);
+      case 3:
+      case 4: return launch_attn<D, 4, false>(p, grid, s, e0, e1);
       default: return -1;
     }
   } else if constexpr (D == 128) {
