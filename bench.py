@@ -301,7 +301,7 @@ def time_prefill(dev, iters: int = 20):
     flop = 4.0 * hq * d * n_req * q_len * (q_len + 1) / 2
     tflops = flop / (us * 1e-6) / 1e12
     return {"workload": "prefill, 4 x 4096 causal rows, 32/8 heads, head_dim 128, bf16",
-            "kernel": "attn_bf16_kernel<128, 8, true, 64, 1, false>", "us": us, "flop": flop,
+            "kernel": "attn_bf16_kernel<128, 4, true, 32, 1, false>", "us": us, "flop": flop,
             "TFLOPs": tflops, "peak_TFLOPs": 2500.0, "frac": tflops / 2500.0,
             "status": int(st.item())}
 

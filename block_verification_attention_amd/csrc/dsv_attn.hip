@@ -22,15 +22,17 @@
 // is split into chunks processed by separate workgroups and merged by log-sum-exp weights in
 // a second, deterministic kernel.
 //
-// Prefill kernel: the same tile machinery with 8 waves stacked along the query rows of one
+// Prefill kernel: the same tile machinery with its waves stacked along the query rows of one
 // head, giving a 128-row tile (the hardware-selected wide tile of the pages) so that every
-// KV tile staged in LDS feeds 128 query rows.
+// KV tile staged in LDS feeds 128 query rows: at head_dim 128 four waves of two 16-row query
+// tiles each (every K and V operand read from LDS feeds two MFMAs), at head_dim 64 eight
+// waves of one.
 //
-// LDS layouts (bf16):
-//   sK  [64][D]  row-major; 16-byte column slots XOR-swizzled by (row & 15) so that the 16
+// LDS layouts (bf16), one K and one V tile per stage:
+//   K [TILE][D]  row-major; 16-byte column slots XOR-swizzled by (row & 15) so that the 16
 //                rows an MFMA operand read touches fall in distinct banks.
-//   sVt [D][64]  V transposed; 8-byte slots (4 KV rows) XOR-swizzled by a function of d that
-//                keeps both the transposing writes and the operand reads conflict-free.
+//   V [TILE][D]  row-major; 32-byte column blocks XOR-swizzled by (row & 7), read with the
+//                transposing LDS loads that form the P.V operand (keys along its K dimension).
 #include <math.h>
 
 #include <atomic>
@@ -47,10 +49,15 @@ constexpr int kXcds = 8;     // dispatch places block b on XCD b % 8
 // Waves with at most this many 16-byte loads per tile stage two tiles in registers (more
 // would push the hot shapes past the register budget of two waves per SIMD).
 constexpr int kTwoSetMaxLoads = 4;
-// Prefill: waves per workgroup, 16 query rows each (128-row tile; 64 rows at head_dim 256,
-// whose wave needs the whole register file for its 16 x 256 output and query fragments).
-constexpr int pf_waves(int D) { return D >= 256 ? 4 : 8; }
-constexpr int pf_rows(int D) { return pf_waves(D) * 16; }
+// Prefill: waves per workgroup and 16-row query tiles per wave (128-row tile; 64 rows at
+// head_dim 256, whose wave needs the whole register file for its 16 x 256 output and query
+// fragments).  At head_dim 128 a wave holds two query tiles, so that every K and V operand it
+// reads from LDS feeds two MFMAs.
+constexpr int pf_qtiles(int D) { return D == 128 ? 2 : 1; }
+constexpr int pf_waves(int D) { return D >= 128 ? 4 : 8; }
+constexpr int pf_rows(int D) { return pf_waves(D) * 16 * pf_qtiles(D); }
+// Prefill KV tile rows at head_dim 128 (the two query tiles double the score registers).
+constexpr int kPfTile128 = 32;
 
 struct AttnParams {
   void *k_pool, *v_pool;
@@ -204,8 +211,8 @@ constexpr float kRescaleSlack = 8.0f;
 
 // ---------------------------------------------------------------------------
 // bf16 MFMA attention kernel.  PF = false: verification (NW = G waves, one 16-row query
-// tile per query head, split KV).  PF = true: prefill (NW = 8 waves along the query rows of
-// one head).  KV tiles of TILE rows stream through an NSTAGE-deep LDS ring.
+// tile per query head, split KV).  PF = true: prefill (NW waves of QT 16-row query tiles
+// along the query rows of one head).  KV tiles of TILE rows stream through an LDS ring.
 // ---------------------------------------------------------------------------
 template <int D, int NW, bool PF>
 constexpr int waves_per_eu_hint() {
@@ -231,6 +238,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
   static_assert(NW % HV == 0, "wave halves");
   constexpr int DB = D / 16;
   constexpr int KS = D / 32;
+  constexpr int QT = PF ? pf_qtiles(D) : 1;  // 16-row query tiles per wave
+  static_assert(QT == 1 || HV == 1, "two query tiles: prefill only");
   static_assert(TILE % 32 == 0 && TILE % RPC == 0, "tile shape");
 
   extern __shared__ __align__(16) uint16_t lds[];
@@ -405,29 +414,33 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
       if (tid == 0 && b == 0 && h == 0) status_or(p.status, bad);
       return;
     }
-    row0 = b * (NW * 16);
+    row0 = b * (NW * 16 * QT);
     if (row0 >= ql) return;
     nrows = ql;
     r_lo = 0;
-    r_hi = c + min(row0 + NW * 16, ql);
+    r_hi = c + min(row0 + NW * 16 * QT, ql);
     q_row0 = qs;
     qsrc = static_cast<const uint16_t *>(p.pf_q);
   }
   (void)n_splits_i;
 
   // ---- query fragment (B operand of S^T = K Q^T): row lq, columns 32ks + 8lg .. +7 ----
-  const int my_row = PF ? row0 + w * 16 + lq : col_row;  // query row index within the request
-  bf16x8 qf[KS];
-  {
+  // query row index within the request of this lane's column in query tile 0 (tile qt: + 16 qt)
+  const int my_row0 = PF ? row0 + w * 16 * QT + lq : col_row;
+  bf16x8 qf[QT][KS];
+  int lim[QT];  // last visible position of this lane's query row in each tile
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int my_row = my_row0 + 16 * qt;
     const bool ok = my_row < nrows && col_ok;
     const uint16_t *qp = qsrc + ((q_row0 + (ok ? my_row : 0)) * p.hq + h) * (int64_t)D + 8 * lg;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const u32x4 v = ok ? gload<u32x4>(qp + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
-      qf[ks] = __builtin_bit_cast(bf16x8, v);
+      qf[qt][ks] = __builtin_bit_cast(bf16x8, v);
     }
+    lim[qt] = c + my_row;
   }
-  const int lim = c + my_row;  // last visible position of this lane's query row
 
   // ---- tile loads: wave w moves pieces q = w, w + NW, ... of the 2 * NCK per tile (piece q
   // < NCK: K rows RPC q .. + RPC - 1, else the same rows of V; 16 bytes per lane) ----
@@ -576,88 +589,111 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
                  v_slot<D>(row, 2 * db + ((lq & 3) >> 1)) * 16 + 8 * (lq & 1);
   }
 
-  f32x4 acc_o[DB];
+  f32x4 acc_o[QT][DB];
+  float m_ref[QT], l_run[QT];  // reference max (log2 units) and row-sum partial
 #pragma unroll
-  for (int db = 0; db < DB; ++db) acc_o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY, l_run = 0.f;  // reference max (log2 units) and row-sum partial
+  for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc_o[qt][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_ref[qt] = -INFINITY;
+    l_run[qt] = 0.f;
+  }
 
   const int n_tiles = (t_hi - r_lo + HV * TILE - 1) / (HV * TILE);  // stages of HV tiles
-  const int wave_row_lo = PF ? row0 + w * 16 : 0;
+  const int wave_row_lo = PF ? row0 + w * 16 * QT : 0;  // first query row of the wave
+  constexpr int WROWS = 16 * QT;                        // query rows per wave
   const bool wave_live = wave_row_lo < nrows && wave_has_heads;
   const float sl2 = p.scale_log2;
 
-  // S^T blocks of one tile from LDS stage STAGE: acc_s[kb][e] = raw score of KV row
-  // base + 16kb + 4lg + e for query row lq (KB = the tile's rows / 16)
+  // S^T blocks of one tile from LDS stage STAGE: acc_s[qt][kb][e] = raw score of KV row
+  // base + 16kb + 4lg + e for query row lq of query tile qt (KB = the tile's rows / 16); each
+  // K operand read feeds the QT query tiles
   auto tile_qk = [&](auto stage_c, auto &acc_s) __attribute__((always_inline)) {
     constexpr int STAGE = decltype(stage_c)::value;
-    constexpr int KB = std::extent<std::remove_reference_t<decltype(acc_s)>>::value;
+    constexpr int KB = std::extent<std::remove_reference_t<decltype(acc_s)>, 1>::value;
 #pragma unroll
     for (int kbk = 0; kbk < KB; ++kbk) {
-      acc_s[kbk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) acc_s[qt][kbk] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const uint32_t a_addr = koff[ks] + STAGE * STAGE_BYTES + 16 * kbk * (2 * D);
         const bf16x8 a = __builtin_bit_cast(bf16x8, *(lds_u4 *)(uintptr_t)a_addr);
-        acc_s[kbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], acc_s[kbk], 0, 0, 0);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          acc_s[qt][kbk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qt][ks], acc_s[qt][kbk], 0, 0, 0);
       }
     }
   };
   // Online softmax of those scores (positions at or past hi or past the row's last visible
   // position masked with MASK) and P.V from the same stage.
-  auto tile_softmax_pv = [&](int base, int hi, auto stage_c, auto mask_c, auto &acc_s) __attribute__((always_inline)) {
+  auto tile_softmax_pv = [&](int base, int hi, auto stage_c, auto mask_c, auto &acc_s, auto &&mid) __attribute__((always_inline)) {
     constexpr int STAGE = decltype(stage_c)::value;
-    constexpr bool MASK = decltype(mask_c)::value;
-    constexpr int KB = std::extent<std::remove_reference_t<decltype(acc_s)>>::value;
+    const bool masked = mask_c;  // a compile-time constant, or a wave-uniform flag
+    constexpr int KB = std::extent<std::remove_reference_t<decltype(acc_s)>, 1>::value;
     constexpr int KK = KB / 2;  // 32-row P.V steps
-    float mt = -INFINITY;  // this lane's maximum over its entries of the row
+    float m_use[QT];
 #pragma unroll
-    for (int kbk = 0; kbk < KB; ++kbk)
+    for (int qt = 0; qt < QT; ++qt) {
+      if (masked) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (MASK) {
-          const int pos = base + 16 * kbk + 4 * lg + e;
-          acc_s[kbk][e] = (pos < hi && pos <= lim) ? acc_s[kbk][e] : -INFINITY;
-        }
-        mt = fmaxf(mt, acc_s[kbk][e]);
+        for (int kbk = 0; kbk < KB; ++kbk)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int pos = base + 16 * kbk + 4 * lg + e;
+            acc_s[qt][kbk][e] = (pos < hi && pos <= lim[qt]) ? acc_s[qt][kbk][e] : -INFINITY;
+          }
       }
-    // The reference moves only when some entry of a row exceeds it by more than the slack.
-    // Whether any does is decided per lane (a ballot); the row maximum over the four lanes
-    // holding the row is formed only then.
-    if (__builtin_expect(__any(mt * sl2 > m_ref + kRescaleSlack), 0)) {
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mt2 = mt * sl2;  // row maximum of the tile in log2 units (-inf if masked)
-      const float m_new = mt2 > m_ref + kRescaleSlack ? mt2 : m_ref;
-      // rows that have seen no visible key yet hold zeros: their factor is 0 (not NaN)
-      const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-      m_ref = m_new;
-      l_run *= alpha;
+      float mt = -INFINITY;  // this lane's maximum over its entries of the row
 #pragma unroll
-      for (int db = 0; db < DB; ++db) acc_o[db] *= alpha;
+      for (int kbk = 0; kbk < KB; ++kbk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mt = fmaxf(mt, acc_s[qt][kbk][e]);
+      // The reference moves only when some entry of a row exceeds it by more than the slack.
+      // Whether any does is decided per lane (a ballot); the row maximum over the four lanes
+      // holding the row is formed only then.
+      if (__builtin_expect(__any(mt * sl2 > m_ref[qt] + kRescaleSlack), 0)) {
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float mt2 = mt * sl2;  // row maximum of the tile in log2 units (-inf if masked)
+        const float m_new = mt2 > m_ref[qt] + kRescaleSlack ? mt2 : m_ref[qt];
+        // rows that have seen no visible key yet hold zeros: their factor is 0 (not NaN)
+        const float alpha = m_ref[qt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref[qt] - m_new);
+        m_ref[qt] = m_new;
+        l_run[qt] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc_o[qt][db] *= alpha;
+      }
+      m_use[qt] = m_ref[qt] == -INFINITY ? 0.f : m_ref[qt];
     }
-    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+    mid();
     // P (bf16) is the B operand of O^T = V^T P^T; the row sum accumulates the fp32 values
-    uint32_t pb[KB][2];
+    uint32_t pb[QT][KB][2];
 #pragma unroll
-    for (int kbk = 0; kbk < KB; ++kbk) {
-      float pe[4];
+    for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc_s[kbk][e], sl2, -m_use));
-        l_run += pe[e];
+      for (int kbk = 0; kbk < KB; ++kbk) {
+        float pe[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc_s[qt][kbk][e], sl2, -m_use[qt]));
+          l_run[qt] += pe[e];
+        }
+        pb[qt][kbk][0] = cvt_pk_bf16(pe[0], pe[1]);
+        pb[qt][kbk][1] = cvt_pk_bf16(pe[2], pe[3]);
       }
-      pb[kbk][0] = cvt_pk_bf16(pe[0], pe[1]);
-      pb[kbk][1] = cvt_pk_bf16(pe[2], pe[3]);
-    }
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      const bf16x8 b = __builtin_bit_cast(
-          bf16x8, make_uint4(pb[2 * kk][0], pb[2 * kk][1], pb[2 * kk + 1][0], pb[2 * kk + 1][1]));
+      bf16x8 b[QT];
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt)
+        b[qt] = __builtin_bit_cast(bf16x8, make_uint4(pb[qt][2 * kk][0], pb[qt][2 * kk][1],
+                                                      pb[qt][2 * kk + 1][0], pb[qt][2 * kk + 1][1]));
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         // transposing reads: lane j of each 16-lane group receives V[R + t][16db + j], t < 4,
         // from the 8-byte chunks that lanes j/4 + 4t point at (rows R + lq/4, columns
-        // 16db + 4(lq%4)); R = 32kk + 16half + 4lg.
+        // 16db + 4(lq%4)); R = 32kk + 16half + 4lg.  Each V operand feeds the QT query tiles.
         const uint32_t v0 = voffs[db] + STAGE * STAGE_BYTES + (32 * kk) * (2 * D);
         const auto lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(uintptr_t)v0);
         const auto hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(uintptr_t)(v0 + 16 * (2 * D)));
@@ -667,7 +703,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
           a[e] = lo[e];
           a[4 + e] = hi[e];
         }
-        acc_o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc_o[db], 0, 0, 0);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+          acc_o[qt][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[qt], acc_o[qt][db], 0, 0, 0);
       }
     }
   };
@@ -675,16 +713,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
   // LDS stage STAGE; with MASK, positions at or past hi or past the row's last visible position
   // are excluded.
   auto compute_tile = [&](int base, int hi, auto stage_c, auto mask_c, auto rows_c) __attribute__((always_inline)) {
-    f32x4 acc_s[decltype(rows_c)::value / 16];
+    f32x4 acc_s[QT][decltype(rows_c)::value / 16];
     tile_qk(stage_c, acc_s);
-    tile_softmax_pv(base, hi, stage_c, mask_c, acc_s);
+    tile_softmax_pv(base, hi, stage_c, mask_c, acc_s, [] {});
   };
 
   // rows of this wave that can see any key of tile `base`; interior tiles skip the mask
   auto consume = [&](int stage_base, auto stage_c) __attribute__((always_inline)) {
     const int base = stage_base + half * TILE;
     if (HV > 1 && base >= t_hi) return;                     // this half's tile is past the range
-    if (!wave_live || base > c + wave_row_lo + 15) return;  // past every row's last position
+    if (!wave_live || base > c + wave_row_lo + WROWS - 1) return;  // past every row's last position
     using Rows = std::integral_constant<int, TILE>;
     if (base + TILE - 1 <= c + wave_row_lo && base + TILE <= t_hi)
       compute_tile(base, t_hi, stage_c, std::integral_constant<bool, false>{}, Rows{});
@@ -742,27 +780,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     // tile t + 2 is stored into the third stage; one barrier per tile.  Tile t sits in stage
     // t % 3 and its scores in buffer t % 2 (the loop is unrolled by 6).
     constexpr int KB = TILE / 16;
-    f32x4 sa[KB], sb[KB];
-    auto live = [&](int t) __attribute__((always_inline)) {
-      return wave_live && r_lo + t * TILE <= c + wave_row_lo + 15;
-    };
+    f32x4 sa[QT][KB], sb[QT][KB];
+    // Every wave computes every tile (a wave whose rows end before a tile sees it fully masked,
+    // and waves past the request work on zero queries that are never stored), so that the
+    // iteration has no branch but the mask choice before the row maximum and the rare
+    // reference move: the next tile's Q.K products share one basic block with this tile's
+    // exponentials and P.V, free to interleave.  The tile after the last is never consumed.
     if (n_tiles > 0) load_tile(r_lo, xa);
     if (n_tiles > 1) load_tile(r_lo + TILE, xb);
     if (n_tiles > 0) store_tile(xa, 0);
     if (n_tiles > 1) store_tile(xb, 1);
     if (n_tiles > 2) load_tile(r_lo + 2 * TILE, xa);
     __syncthreads();
-    if (n_tiles > 0 && live(0)) tile_qk(std::integral_constant<int, 0>{}, sa);
+    tile_qk(std::integral_constant<int, 0>{}, sa);
     auto iter = [&](int t, auto s_c, auto &cur, auto &nxt) __attribute__((always_inline)) {
       constexpr int S = decltype(s_c)::value;
-      if (t + 1 < n_tiles && live(t + 1)) tile_qk(std::integral_constant<int, (S + 1) % 3>{}, nxt);
-      if (live(t)) {
-        const int base = r_lo + t * TILE;
-        if (base + TILE - 1 <= c + wave_row_lo && base + TILE <= t_hi)
-          tile_softmax_pv(base, t_hi, s_c, std::integral_constant<bool, false>{}, cur);
-        else
-          tile_softmax_pv(base, t_hi, s_c, std::integral_constant<bool, true>{}, cur);
-      }
+      const int base = r_lo + t * TILE;
+      // unmasked when every position of the tile is visible to every row of the wave
+      const bool masked = !(base + TILE - 1 <= c + wave_row_lo && base + TILE <= t_hi);
+      tile_softmax_pv(base, t_hi, s_c, masked, cur,
+                      [&] { tile_qk(std::integral_constant<int, (S + 1) % 3>{}, nxt); });
       if (t + 2 < n_tiles) {
         if (t + 3 < n_tiles)
           store_load_tile(xa, (S + 2) % 3, r_lo + (t + 3) * TILE);
@@ -884,55 +921,64 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) xs[at(4 * db + e)] = acc_o[db][e];
-      xs[at(4 * DB)] = m_ref;
-      xs[at(4 * DB + 1)] = l_run;
+        for (int e = 0; e < 4; ++e) xs[at(4 * db + e)] = acc_o[0][db][e];
+      xs[at(4 * DB)] = m_ref[0];
+      xs[at(4 * DB + 1)] = l_run[0];
     }
     __syncthreads();
     if (half == 1) return;
     const float m1 = xs[at(4 * DB)], l1 = xs[at(4 * DB + 1)];
-    const float m_new = fmaxf(m_ref, m1);
-    const float a0 = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+    const float m_new = fmaxf(m_ref[0], m1);
+    const float a0 = m_ref[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref[0] - m_new);
     const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m_new);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc_o[db][e] = acc_o[db][e] * a0 + xs[at(4 * db + e)] * a1;
-    l_run = l_run * a0 + l1 * a1;
-    m_ref = m_new;
+      for (int e = 0; e < 4; ++e) acc_o[0][db][e] = acc_o[0][db][e] * a0 + xs[at(4 * db + e)] * a1;
+    l_run[0] = l_run[0] * a0 + l1 * a1;
+    m_ref[0] = m_new;
   }
   if (!wave_live) return;
-  // full row sum across the four lane groups holding the row
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  if (my_row >= nrows || !col_ok) return;
-  const bool empty = !(l_run > 0.f);
-  const float inv_l = empty ? 0.f : 1.f / l_run;
-  const float lse_v = empty ? -INFINITY : (m_ref + __builtin_amdgcn_logf(l_run)) * 0.69314718055994530942f;
-  const int64_t orow = q_row0 + my_row;
-  if (PF || n_splits_i == 1) {
-    uint16_t *o = static_cast<uint16_t *>(PF ? p.pf_out : p.out) + (orow * p.hq + h) * (int64_t)D;
+  // full row sums across the four lane groups holding each row
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int d = 16 * db + 4 * lg;
-      gstore(o + d, u32x2{cvt_pk_bf16(acc_o[db][0] * inv_l, acc_o[db][1] * inv_l),
-                          cvt_pk_bf16(acc_o[db][2] * inv_l, acc_o[db][3] * inv_l)});
-    }
-    float *lse = PF ? p.pf_lse : p.lse;
-    if (lse && lg == 0) gstore(lse + orow * p.hq + h, lse_v);
-  } else {
-    // partials are read once, by the merge kernel: streaming (non-temporal) stores, rounded to
-    // bf16 like the output itself (half the bytes of the write-back and of the merge's reads;
-    // the merge weights and sums them in fp32)
-    uint16_t *o = p.ws_o + (((int64_t)split * p.m_bs + orow) * p.hq + h) * D;
+  for (int qt = 0; qt < QT; ++qt) {
+    l_run[qt] += __shfl_xor(l_run[qt], 16);
+    l_run[qt] += __shfl_xor(l_run[qt], 32);
+  }
+  if (!col_ok) return;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int d = 16 * db + 4 * lg;
-      gstore_stream(o + d, u32x2{cvt_pk_bf16(acc_o[db][0] * inv_l, acc_o[db][1] * inv_l),
-                                 cvt_pk_bf16(acc_o[db][2] * inv_l, acc_o[db][3] * inv_l)});
+  for (int qt = 0; qt < QT; ++qt) {
+    const int my_row = my_row0 + 16 * qt;
+    if (my_row >= nrows) break;
+    const bool empty = !(l_run[qt] > 0.f);
+    const float inv_l = empty ? 0.f : 1.f / l_run[qt];
+    const float lse_v = empty ? -INFINITY : (m_ref[qt] + __builtin_amdgcn_logf(l_run[qt])) * 0.69314718055994530942f;
+    const int64_t orow = q_row0 + my_row;
+    const f32x4 *ao = acc_o[qt];
+    if (PF || n_splits_i == 1) {
+      uint16_t *o = static_cast<uint16_t *>(PF ? p.pf_out : p.out) + (orow * p.hq + h) * (int64_t)D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int d = 16 * db + 4 * lg;
+        gstore(o + d, u32x2{cvt_pk_bf16(ao[db][0] * inv_l, ao[db][1] * inv_l),
+                            cvt_pk_bf16(ao[db][2] * inv_l, ao[db][3] * inv_l)});
+      }
+      float *lse = PF ? p.pf_lse : p.lse;
+      if (lse && lg == 0) gstore(lse + orow * p.hq + h, lse_v);
+    } else {
+      // partials are read once, by the merge kernel: streaming (non-temporal) stores, rounded
+      // to bf16 like the output itself (half the bytes of the write-back and of the merge's
+      // reads; the merge weights and sums them in fp32)
+      uint16_t *o = p.ws_o + (((int64_t)split * p.m_bs + orow) * p.hq + h) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int d = 16 * db + 4 * lg;
+        gstore_stream(o + d, u32x2{cvt_pk_bf16(ao[db][0] * inv_l, ao[db][1] * inv_l),
+                                   cvt_pk_bf16(ao[db][2] * inv_l, ao[db][3] * inv_l)});
+      }
+      if (lg == 0)
+        gstore_stream(p.ws_lse + ((int64_t)split * p.m_bs + orow) * p.hq + h, lse_v);
     }
-    if (lg == 0)
-      gstore_stream(p.ws_lse + ((int64_t)split * p.m_bs + orow) * p.hq + h, lse_v);
   }
 }
 
@@ -1277,7 +1323,7 @@ static bool launch_attn_k(const AttnParams &p, int grid, hipStream_t s, hipEvent
   // the two-waves-per-head verification kernel takes 64-row tiles when a tile's wave loads
   // split evenly over its waves (fewer, longer stages; otherwise the uneven piece pattern
   // spills)
-  constexpr int TILE = TileCfg<D>::TILE;
+  constexpr int TILE = (PF && D == 128) ? kPfTile128 : TileCfg<D>::TILE;
   constexpr size_t shm = (size_t)(PF ? 3 : 2) * HV * 2 * TILE * D * sizeof(uint16_t);
   auto kern = attn_bf16_kernel<D, NW, PF, TILE, HV, MAP>;
   // once per kernel (idempotent), so that a captured call contains launches only
