@@ -42,9 +42,9 @@ PROFILED_KERNEL = "attn_bf16_kernel<128, 8, false, 64, 2, false>"
 # WRITE_SIZE runs (profiles/attn_verify_cfg3_hbm_traffic.md, calibrated there against the
 # streaming-read probe and a pool copy), valid for the kernel source with this SHA-256 only.
 COUNTED_SOURCE = ("block_verification_attention_amd/csrc/dsv_attn.hip",
-                  "a0b6f4c79f27373deb8153afd917ac2afe075f11b5c258e9d276e44de0c02e6d")
-COUNTED_READ_BYTES = 270_437_680
-COUNTED_WRITE_BYTES = 6_161_787
+                  "fc234e8b692a7bc8565250b5787028762b5eb630b50ce9622b305ee44b74e1a5")
+COUNTED_READ_BYTES = 270_420_563
+COUNTED_WRITE_BYTES = 5_519_575
 
 
 def counted_traffic():
@@ -603,6 +603,8 @@ def main():
                     help="only time the CPU oracle on every configuration (1 and all host threads)")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="launch each step's calls directly instead of replaying a captured HIP graph")
+    ap.add_argument("--only", choices=["prefill", "other_verify"], default=None,
+                    help="only run that section, `--steps` times, and print its JSON (for counter runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "dsv runs on one GPU: splitting a step over several GPUs "
@@ -621,6 +623,12 @@ def main():
         print(json.dumps(cpu_configs(dev)))
         return
     dsv.load_library()
+    if args.only == "prefill":
+        print(json.dumps(time_prefill(dev, iters=args.steps)))
+        return
+    if args.only == "other_verify":
+        print(json.dumps(time_other_verify(dev, HipEvents(), iters=args.steps)))
+        return
     c = wl.config3()
 
     def to_dev(a):

@@ -633,6 +633,32 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     constexpr int KB = std::extent<std::remove_reference_t<decltype(acc_s)>, 1>::value;
     constexpr int KK = KB / 2;  // 32-row P.V steps
     float m_use[QT];
+    // transposing reads: lane j of each 16-lane group receives V[R + t][16db + j], t < 4, from
+    // the 8-byte chunks that lanes j/4 + 4t point at (rows R + lq/4, columns 16db + 4(lq%4));
+    // R = 32kk + 16half + 4lg.  Each V operand feeds the QT query tiles.
+    auto v_operand = [&](int kk, int db) __attribute__((always_inline)) {
+      const uint32_t v0 = voffs[db] + STAGE * STAGE_BYTES + (32 * kk) * (2 * D);
+      const auto lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(uintptr_t)v0);
+      const auto hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(uintptr_t)(v0 + 16 * (2 * D)));
+      bf16x8 a;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[e] = lo[e];
+        a[4 + e] = hi[e];
+      }
+      return a;
+    };
+    // prefill (one 32-row step per tile): the tile's V operands are read first, so
+    // that their LDS latency runs behind the row maximum, the next tile's Q.K and the
+    // exponentials
+    constexpr int VPRE = PF ? KK * DB : 1;
+    bf16x8 va[VPRE];
+    if constexpr (PF) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) va[kk * DB + db] = v_operand(kk, db);
+    }
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
       if (masked) {
@@ -691,18 +717,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
                                                       pb[qt][2 * kk + 1][0], pb[qt][2 * kk + 1][1]));
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        // transposing reads: lane j of each 16-lane group receives V[R + t][16db + j], t < 4,
-        // from the 8-byte chunks that lanes j/4 + 4t point at (rows R + lq/4, columns
-        // 16db + 4(lq%4)); R = 32kk + 16half + 4lg.  Each V operand feeds the QT query tiles.
-        const uint32_t v0 = voffs[db] + STAGE * STAGE_BYTES + (32 * kk) * (2 * D);
-        const auto lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(uintptr_t)v0);
-        const auto hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(uintptr_t)(v0 + 16 * (2 * D)));
         bf16x8 a;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a[e] = lo[e];
-          a[4 + e] = hi[e];
-        }
+        if constexpr (PF)
+          a = va[kk * DB + db];
+        else
+          a = v_operand(kk, db);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
           acc_o[qt][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[qt], acc_o[qt][db], 0, 0, 0);
