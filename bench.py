@@ -43,8 +43,8 @@ PROFILED_KERNEL = "attn_bf16_kernel<128, 8, false, 64, 2, false>"
 # streaming-read probe and a pool copy), valid for the kernel source with this SHA-256 only.
 COUNTED_SOURCE = ("block_verification_attention_amd/csrc/dsv_attn.hip",
                   "fc234e8b692a7bc8565250b5787028762b5eb630b50ce9622b305ee44b74e1a5")
-COUNTED_READ_BYTES = 270_420_563
-COUNTED_WRITE_BYTES = 5_519_575
+COUNTED_READ_BYTES = 270_462_312
+COUNTED_WRITE_BYTES = 5_521_889
 
 
 def counted_traffic():
