@@ -376,14 +376,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     // that share the K and V operands, so a request with k_i rows fills a tile with
     // 16 / R heads of R rows (R = k_i rounded up to a power of two).  The workgroup's waves
     // then take 16 / R heads each and those left without a head skip the tile arithmetic.
+    // Where a KV head's query heads are spread over several workgroups (HG > 1), a request
+    // whose packed tiles hold more heads needs fewer of them: its heads are regrouped as
+    // evenly as possible over ceil(G / (16 / R waves' heads)) workgroups and the grid's other
+    // head-group workgroups of the request leave, so that fewer of them stream its KV rows.
     int R = 1;
     while (R < ki) R <<= 1;
+    int gw = p.GW, hb = hg * p.GW;  // heads of this workgroup: [G g + hb, + gw)
+    if (p.HG > 1) {
+      const int cap = NWH * (16 / R);
+      const int hgr = (p.G + cap - 1) / cap;
+      if (hg >= hgr) return;
+      gw = (p.G + hgr - 1) / hgr;
+      hb = hg * gw;
+    }
     const int slot = wh * (16 / R) + lq / R;  // head slot of this lane's column
-    const int heads_here = min(p.GW, p.G - hg * p.GW);  // the last group may be partial
+    const int heads_here = min(gw, p.G - hb);  // the last group may be partial
     col_ok = slot < heads_here;
     col_row = lq % R;
     wave_has_heads = wh * (16 / R) < heads_here;
-    h = h0 + (col_ok ? slot : 0);
+    h = g * p.G + hb + (col_ok ? slot : 0);
     if (p.k_new) {
       knew = static_cast<const uint16_t *>(p.k_new);
       vnew = static_cast<const uint16_t *>(p.v_new);
