@@ -42,7 +42,7 @@ PROFILED_KERNEL = "attn_bf16_kernel<128, 8, false, 64, 2, false>"
 # WRITE_SIZE runs (profiles/attn_verify_cfg3_hbm_traffic.md, calibrated there against the
 # streaming-read probe and a pool copy), valid for the kernel source with this SHA-256 only.
 COUNTED_SOURCE = ("block_verification_attention_amd/csrc/dsv_attn.hip",
-                  "b655ac056ac3cf0204586d0bb7126c33bb5cb3a0f97208dea5e5a0e1b6f3451f")
+                  "19fcfba23f55882cbf54f25c33b9c1524aad4d4a575b3f9a4d7794a92e492176")
 COUNTED_READ_BYTES = 270_446_219
 COUNTED_WRITE_BYTES = 5_528_330
 

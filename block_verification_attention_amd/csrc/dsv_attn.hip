@@ -637,8 +637,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
       }
     }
   };
-  // Online softmax of those scores (positions at or past hi or past the row's last visible
-  // position masked with MASK) and P.V from the same stage.
+  // Online softmax of those scores and P.V from the same stage.  With mask_c (a compile-time
+  // constant or a wave-uniform flag), positions at or past hi or past the row's last visible
+  // position are excluded; `mid` runs between the row maximum and the exponentials (the
+  // prefill loop puts the next tile's Q.K products there).
   auto tile_softmax_pv = [&](int base, int hi, auto stage_c, auto mask_c, auto &acc_s, auto &&mid) __attribute__((always_inline)) {
     constexpr int STAGE = decltype(stage_c)::value;
     const bool masked = mask_c;  // a compile-time constant, or a wave-uniform flag
@@ -741,8 +743,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     }
   };
   // One tile of ROWS (TILE, or 32 for the candidate block) KV rows at positions base.. from
-  // LDS stage STAGE; with MASK, positions at or past hi or past the row's last visible position
-  // are excluded.
+  // LDS stage STAGE; with mask_c, positions at or past hi or past the row's last visible
+  // position are excluded.
   auto compute_tile = [&](int base, int hi, auto stage_c, auto mask_c, auto rows_c) __attribute__((always_inline)) {
     f32x4 acc_s[QT][decltype(rows_c)::value / 16];
     tile_qk(stage_c, acc_s);
