@@ -42,9 +42,9 @@ PROFILED_KERNEL = "attn_bf16_kernel<128, 8, false, 64, 2, false>"
 # WRITE_SIZE runs (profiles/attn_verify_cfg3_hbm_traffic.md, calibrated there against the
 # streaming-read probe and a pool copy), valid for the kernel source with this SHA-256 only.
 COUNTED_SOURCE = ("block_verification_attention_amd/csrc/dsv_attn.hip",
-                  "19fcfba23f55882cbf54f25c33b9c1524aad4d4a575b3f9a4d7794a92e492176")
-COUNTED_READ_BYTES = 270_446_219
-COUNTED_WRITE_BYTES = 5_528_330
+                  "88aa21c911f340f37f2908f5d29fc4a8eb24950e8de099c0a0e5ef3e9769dbef")
+COUNTED_READ_BYTES = 270_444_458
+COUNTED_WRITE_BYTES = 5_518_152
 
 
 def counted_traffic():
@@ -301,7 +301,7 @@ def time_prefill(dev, iters: int = 20):
     flop = 4.0 * hq * d * n_req * q_len * (q_len + 1) / 2
     tflops = flop / (us * 1e-6) / 1e12
     return {"workload": "prefill, 4 x 4096 causal rows, 32/8 heads, head_dim 128, bf16",
-            "kernel": "attn_bf16_kernel<128, 4, true, 32, 1, false>", "us": us, "flop": flop,
+            "kernel": "attn_bf16_kernel<128, 8, true, 32, 1, false>", "us": us, "flop": flop,
             "TFLOPs": tflops, "peak_TFLOPs": 2500.0, "frac": tflops / 2500.0,
             "status": int(st.item())}
 

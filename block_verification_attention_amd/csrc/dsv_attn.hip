@@ -23,10 +23,10 @@
 // a second, deterministic kernel.
 //
 // Prefill kernel: the same tile machinery with its waves stacked along the query rows of one
-// head, giving a 128-row tile (the hardware-selected wide tile of the pages) so that every
-// KV tile staged in LDS feeds 128 query rows: at head_dim 128 four waves of two 16-row query
-// tiles each (every K and V operand read from LDS feeds two MFMAs), at head_dim 64 eight
-// waves of one.
+// head, in 128-row tiles (the hardware-selected wide tile of the pages) so that every KV tile
+// staged in LDS feeds at least 128 query rows: at head_dim 128 eight waves of two 16-row query
+// tiles each, i.e. two 128-row tiles sharing every staged KV tile (and every K and V operand
+// a wave reads from LDS feeds two MFMAs); at head_dim 64 eight waves of one.
 //
 // LDS layouts (bf16), one K and one V tile per stage:
 //   K [TILE][D]  row-major; 16-byte column slots XOR-swizzled by (row & 15) so that the 16
@@ -49,12 +49,12 @@ constexpr int kXcds = 8;     // dispatch places block b on XCD b % 8
 // Waves with at most this many 16-byte loads per tile stage two tiles in registers (more
 // would push the hot shapes past the register budget of two waves per SIMD).
 constexpr int kTwoSetMaxLoads = 4;
-// Prefill: waves per workgroup and 16-row query tiles per wave (128-row tile; 64 rows at
-// head_dim 256, whose wave needs the whole register file for its 16 x 256 output and query
-// fragments).  At head_dim 128 a wave holds two query tiles, so that every K and V operand it
-// reads from LDS feeds two MFMAs.
+// Prefill: waves per workgroup and 16-row query tiles per wave (two 128-row tiles at head_dim
+// 128, one at 64; 64 rows at head_dim 256, whose wave needs the whole register file for its
+// 16 x 256 output and query fragments).  At head_dim 128 a wave holds two query tiles, so that
+// every K and V operand it reads from LDS feeds two MFMAs.
 constexpr int pf_qtiles(int D) { return D == 128 ? 2 : 1; }
-constexpr int pf_waves(int D) { return D >= 128 ? 4 : 8; }
+constexpr int pf_waves(int D) { return D >= 256 ? 4 : 8; }
 constexpr int pf_rows(int D) { return pf_waves(D) * 16 * pf_qtiles(D); }
 // Prefill KV tile rows at head_dim 128 (the two query tiles double the score registers).
 constexpr int kPfTile128 = 32;
