@@ -90,6 +90,16 @@ def test_prefill_ragged(d_head, hq, hkv):
     _run_mixed(c, with_verify=False, tag=f"prefill d{d_head}")
 
 
+def test_prefill_block_edges():
+    # head_dim 128 runs 256-row workgroups of 8 waves x 32 rows on 32-row KV tiles: query
+    # lengths and contexts around those edges (and the 16-row query tiles), so that rows end
+    # inside a wave, a wave's tile or a block, and contexts start the diagonal mid-tile
+    q_len = [1, 15, 16, 17, 31, 32, 33, 255, 256, 257, 511, 513]
+    ctx = [0, 5, 31, 32, 33, 64, 100, 0, 7, 130, 1, 3]
+    c = _prefill_case(61, q_len=q_len, ctx=ctx, hq=8, hkv=2, d=128)
+    _run_mixed(c, with_verify=False, tag="prefill block edges")
+
+
 def test_prefill_fp32():
     c = _prefill_case(57, q_len=[70, 5], ctx=[0, 33], hq=4, hkv=2, d=64, dtype="f32")
     _run_mixed(c, with_verify=False, tag="prefill fp32")
