@@ -50,7 +50,7 @@ def test_bf16_ragged(d_head, hq, hkv, kv_chunk):
 
 @pytest.mark.parametrize("kv_chunk", [0, 128])
 def test_wide_heads_score_jump_sharp_sentinel(kv_chunk):
-    """head_dim 256 with 12 query heads per KV head (head groups, two waves per head): keys
+    """head_dim 256 with 12 query heads per KV head (head groups of up to 4, one wave per head): keys
     deep in a split whose scores jump far above the split's first tile (a query row's own
     direction x 30, so the softmax reference must move); the sharp (queries x 8) and
     leak-detector variants of the same batch run too."""

@@ -1,5 +1,5 @@
 """HIP-graph capture of the calls beyond the greedy step: budget allocator + pack, verification
-attention through a cache map, a head_dim-256 launch with head groups and two waves per head,
+attention through a cache map, a head_dim-256 launch with head groups (one wave per head),
 the sampling-mode verifier on uniforms drawn in the graph by the counter-based generator, and
 the draft confidence features.  One captured graph holds all
 of them; three replays, with eager work and synchronisation between them, reproduce the eager
@@ -35,7 +35,7 @@ def test_next_rows_graph_capture_replays_match_eager():
     out = torch.zeros_like(d["q"])
     lse = torch.zeros((c["m_bs"], c["hq"]), device=DEV)
     ws = torch.zeros(1 << 22, dtype=torch.uint8, device=DEV)
-    # head_dim 256, 6 query heads per KV head (head groups of 3, two waves per head)
+    # head_dim 256, 6 query heads per KV head (head groups of 3, one wave per head)
     c2 = small_case(92, hq=12, hkv=2, d=256, k=(16, 3, 9), ctx=(900, 40, 2100))
     d2 = device_case(c2)
     packed2 = gpu_pack(c2, d2)
