@@ -90,14 +90,23 @@ def test_prefill_ragged(d_head, hq, hkv):
     _run_mixed(c, with_verify=False, tag=f"prefill d{d_head}")
 
 
-def test_prefill_block_edges():
-    # head_dim 128 runs 256-row workgroups of 8 waves x 32 rows on 32-row KV tiles: query
-    # lengths and contexts around those edges (and the 16-row query tiles), so that rows end
-    # inside a wave, a wave's tile or a block, and contexts start the diagonal mid-tile
-    q_len = [1, 15, 16, 17, 31, 32, 33, 255, 256, 257, 511, 513]
-    ctx = [0, 5, 31, 32, 33, 64, 100, 0, 7, 130, 1, 3]
-    c = _prefill_case(61, q_len=q_len, ctx=ctx, hq=8, hkv=2, d=128)
-    _run_mixed(c, with_verify=False, tag="prefill block edges")
+# Query lengths and contexts around each head_dim's tile edges, so that rows end inside a
+# wave, a wave's tile or a workgroup's row block, and contexts start the diagonal mid-tile:
+# head_dim 128 runs 256-row workgroups of 8 waves x 32 rows on 32-row KV tiles; head_dim 64
+# 128-row workgroups of 8 waves x 16 rows on 64-row KV tiles; head_dim 256 64-row workgroups
+# of 4 waves x 16 rows on 32-row KV tiles.
+_EDGES = {
+    128: ([1, 15, 16, 17, 31, 32, 33, 255, 256, 257, 511, 513], [0, 5, 31, 32, 33, 64, 100, 0, 7, 130, 1, 3], 8, 2),
+    64: ([1, 15, 16, 17, 63, 64, 65, 127, 128, 129, 255, 257], [0, 5, 63, 64, 65, 128, 100, 0, 7, 130, 1, 3], 4, 1),
+    256: ([1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 129], [0, 5, 31, 32, 33, 64, 100, 0, 7, 130, 1, 3], 6, 2),
+}
+
+
+@pytest.mark.parametrize("d_head", [128, 64, 256])
+def test_prefill_block_edges(d_head):
+    q_len, ctx, hq, hkv = _EDGES[d_head]
+    c = _prefill_case(61 + d_head, q_len=q_len, ctx=ctx, hq=hq, hkv=hkv, d=d_head)
+    _run_mixed(c, with_verify=False, tag=f"prefill block edges d{d_head}")
 
 
 def test_prefill_fp32():
