@@ -42,9 +42,9 @@ PROFILED_KERNEL = "attn_bf16_kernel<128, 8, false, 64, 2, false>"
 # WRITE_SIZE runs (profiles/attn_verify_cfg3_hbm_traffic.md, calibrated there against the
 # streaming-read probe and a pool copy), valid for the kernel source with this SHA-256 only.
 COUNTED_SOURCE = ("block_verification_attention_amd/csrc/dsv_attn.hip",
-                  "88aa21c911f340f37f2908f5d29fc4a8eb24950e8de099c0a0e5ef3e9769dbef")
-COUNTED_READ_BYTES = 270_444_458
-COUNTED_WRITE_BYTES = 5_518_152
+                  "93cf921d172c22ed26b25d33b65cd2428cf8fad0a3cd9563222d2fb945df3da5")
+COUNTED_READ_BYTES = 270_413_008
+COUNTED_WRITE_BYTES = 5_523_763
 
 
 def counted_traffic():

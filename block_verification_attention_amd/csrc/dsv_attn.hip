@@ -286,9 +286,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
       hg = t0 % p.HG;  // this workgroup's query heads: [G g + GW hg, + GW)
       t0 /= p.HG;
     }
-    const int t = t0;
-    const int i = t % p.n_bs;
-    split = t / p.n_bs;
+    // With fewer KV heads than XCDs a unit's XCD follows its position t0 % n_bs, and with n_bs
+    // a multiple of 8 / hkv it ignores the split, so every split of a request lands on the
+    // same XCD and ragged contexts leave some XCDs far more rows than others (1.7x on the
+    // 32-request head_dim-256 set).  There, position t0 % n_bs of split t0 / n_bs holds
+    // request (t0 + split) % n_bs: the requests rotate by one position per split.  With 8 or
+    // more KV heads every XCD already serves one KV head of every (request, split).
+    split = t0 / p.n_bs;
+    const int i = p.hkv < kXcds ? (t0 % p.n_bs + split) % p.n_bs : t0 % p.n_bs;
     const int h0 = g * p.G + hg * p.GW;
     h = h0 + wh;
     int ki, bad, end;
@@ -1317,10 +1322,13 @@ static Plan make_plan(const dsv_attn_args *a) {
     const int GW = verify_heads_per_wg(a->d, G);
     const int64_t units = (int64_t)a->n_bs * a->hkv * verify_head_groups(a->d, G);
     // wave groups in flight: two per SIMD (512 groups of G waves, or 256 two-half ones); the
-    // wide-head workgroups (4 waves, two per CU at a time) aim at two rounds, whose shorter
-    // splits balance requests of different lengths
+    // wide-head workgroups (4 waves, two per CU at a time) aim at three rounds: the head
+    // groups that per-request regrouping drops at run time (requests of 8 or fewer rows) leave
+    // fewer workgroups than counted here, and a plan for two rounds left 1.3 of them on the
+    // 32-request head_dim-256 set, its sparse second round idling most CUs (197 us against
+    // 165 us for 1.7 rounds)
     const int64_t cus = device_cus();
-    const int64_t wgs = a->d >= 256 ? 4 * cus : 2 * cus / verify_halves(GW);
+    const int64_t wgs = a->d >= 256 ? 6 * cus : 2 * cus / verify_halves(GW);
     int64_t target = (wgs + units - 1) / units;
     if (target < 1) target = 1;
     if (target > 64) target = 64;
