@@ -1,5 +1,5 @@
 // Streaming-read probe: the practical HBM read ceiling against which the verification
-// kernel's bandwidth is judged.  A plain read of a large buffer in the access pattern of the
+// kernel's bandwidth is measured.  A plain read of a large buffer in the access pattern of the
 // verification kernel: each of two workgroups per CU streams one contiguous range in 32 KB
 // blocks (every thread issues eight 16-byte non-temporal loads per block).  A measurement
 // helper, not part of the method.
