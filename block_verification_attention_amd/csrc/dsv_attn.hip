@@ -378,29 +378,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
     q_row0 = off;
     qsrc = static_cast<const uint16_t *>(p.q);
     // Head packing: the 16 columns of a wave's tile are independent (query head, row) pairs
-    // that share the K and V operands, so a request with k_i rows fills a tile with
-    // 16 / R heads of R rows (R = k_i rounded up to a power of two).  The workgroup's waves
-    // then take 16 / R heads each and those left without a head skip the tile arithmetic.
-    // Where a KV head's query heads are spread over several workgroups (HG > 1), a request
-    // whose packed tiles hold more heads needs fewer of them: its heads are regrouped as
-    // evenly as possible over ceil(G / (16 / R waves' heads)) workgroups and the grid's other
-    // head-group workgroups of the request leave, so that fewer of them stream its KV rows.
-    int R = 1;
-    while (R < ki) R <<= 1;
-    int gw = p.GW, hb = hg * p.GW;  // heads of this workgroup: [G g + hb, + gw)
+    // that share the K and V operands.  The request's G k_i pairs of this KV head, pair
+    // p = head k_i + row, fill the columns of the workgroup's waves in order (wave w takes
+    // pairs 16 w .. 16 w + 15), so that a wave's tile holds rows of several heads when k_i < 16
+    // and waves past the last pair skip the tile arithmetic.  Where a KV head's query heads
+    // are spread over several workgroups (HG > 1), the pairs are split as evenly as possible
+    // over ceil(G k_i / (16 waves)) workgroups and the grid's other head-group workgroups of the
+    // request leave, so that fewer of them stream its KV rows.  (With HG = 1 the host plan
+    // gives every workgroup at least ceil(G k_i / 16) <= G waves, so all pairs fit.)
+    const int pairs = p.G * ki;
+    int pb = 0, pe = pairs;  // this workgroup's pairs
     if (p.HG > 1) {
-      const int cap = NWH * (16 / R);
-      const int hgr = (p.G + cap - 1) / cap;
+      const int cap = NWH * 16;
+      const int hgr = (pairs + cap - 1) / cap;
       if (hg >= hgr) return;
-      gw = (p.G + hgr - 1) / hgr;
-      hb = hg * gw;
+      const int per = (pairs + hgr - 1) / hgr;
+      pb = hg * per;
+      pe = min(pairs, pb + per);
     }
-    const int slot = wh * (16 / R) + lq / R;  // head slot of this lane's column
-    const int heads_here = min(gw, p.G - hb);  // the last group may be partial
-    col_ok = slot < heads_here;
-    col_row = lq % R;
-    wave_has_heads = wh * (16 / R) < heads_here;
-    h = g * p.G + hb + (col_ok ? slot : 0);
+    const int pr = pb + wh * 16 + lq;  // this lane's pair
+    col_ok = pr < pe;
+    col_row = col_ok ? pr % ki : 0;
+    wave_has_heads = pb + wh * 16 < pe;
+    h = g * p.G + (col_ok ? pr / ki : 0);
     if (p.k_new) {
       knew = static_cast<const uint16_t *>(p.k_new);
       vnew = static_cast<const uint16_t *>(p.v_new);
