@@ -42,7 +42,7 @@ PROFILED_KERNEL = "attn_bf16_kernel<128, 8, false, 64, 2, false>"
 # WRITE_SIZE runs (profiles/attn_verify_cfg3_hbm_traffic.md, calibrated there against the
 # streaming-read probe and a pool copy), valid for the kernel source with this SHA-256 only.
 COUNTED_SOURCE = ("block_verification_attention_amd/csrc/dsv_attn.hip",
-                  "f984aaf2fe3729a01cc0b6e532a6c8b229543b2aa60f7d745bb886bb53a92dbd")
+                  "7f5d2563aed18812550fa9ad46116ba3eb4433a025e63ef0090834ad016d26e1")
 COUNTED_READ_BYTES = 270_444_171
 COUNTED_WRITE_BYTES = 5_523_292
 

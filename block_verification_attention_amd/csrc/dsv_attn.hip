@@ -1323,7 +1323,7 @@ static Plan make_plan(const dsv_attn_args *a) {
     const int64_t units = (int64_t)a->n_bs * a->hkv * verify_head_groups(a->d, G);
     // wave groups in flight: two per SIMD (512 groups of G waves, or 256 two-half ones); the
     // wide-head workgroups (4 waves, two per CU at a time) aim at three rounds: the head
-    // groups that per-request regrouping drops at run time (requests of 8 or fewer rows) leave
+    // groups that per-request regrouping drops at run time (a request needs ceil(G k_i / 64)) leave
     // fewer workgroups than counted here, and a plan for two rounds left 1.3 of them on the
     // 32-request head_dim-256 set, its sparse second round idling most CUs (197 us against
     // 165 us for 1.7 rounds)
