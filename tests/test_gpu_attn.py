@@ -180,6 +180,42 @@ def test_invalid_requests_flagged_and_zeroed():
     assert torch.isnan(out[off[2]:off[2] + 3].float()).all()
 
 
+@pytest.mark.parametrize("d_head,hq,hkv", [(64, 4, 2), (128, 8, 2), (256, 6, 2)])
+def test_zero_context_requests(d_head, hq, hkv):
+    """Requests with no committed context.  A single anchor (k_i = 1, ctx_i = 0) sees only
+    itself: its probability is exactly 1, so its output is its own value row bit for bit and
+    lse = scale q.k; longer zero-context requests attend over their candidates only (oracle)."""
+    c = small_case(48 + d_head, hq=hq, hkv=hkv, d=d_head, k=(1, 16, 1, 0, 2, 1), ctx=(0, 0, 0, 0, 0, 0))
+    d, packed, out, lse, _ = _run(c, tag=f"zero context d{d_head}")
+    off = packed["offsets"].cpu().numpy()
+    G = hq // hkv
+    q = to_f64(d["q"])
+    kn = to_f64(d["k_new"])
+    for i in np.nonzero(c["k"] == 1)[0]:
+        s = int(off[i])
+        for h in range(hq):
+            assert torch.equal(out[s, h].view(torch.int16), d["v_new"][s, h // G].view(torch.int16)), (i, h)
+            z = float(q[s, h] @ kn[s, h // G]) / np.sqrt(d_head)
+            assert abs(float(lse[s, h]) - z) <= 1e-3, (i, h, float(lse[s, h]), z)
+
+
+def test_all_requests_inactive():
+    """Every k_i = 0: nothing is attended, every row is a tail row (zero output, lse -inf)
+    and the pool is left as it was."""
+    c = small_case(49, k=(0, 0, 0, 0), ctx=(40, 0, 700, 3), extra_tail=8)
+    d = device_case(c)
+    packed = gpu_pack(c, d)
+    assert int(packed["offsets"][-1].item()) == 0
+    k_pool0, v_pool0 = d["k_pool"].clone(), d["v_pool"].clone()
+    out, lse = gpu_attn(c, d, packed, kv_chunk=64)
+    torch.cuda.synchronize()
+    assert int(d["status"].item()) == 0
+    assert torch.all(out.float() == 0)
+    assert torch.all(torch.isneginf(lse))
+    assert torch.equal(d["k_pool"].view(torch.int16), k_pool0.view(torch.int16))
+    assert torch.equal(d["v_pool"].view(torch.int16), v_pool0.view(torch.int16))
+
+
 def test_context_beyond_plan_is_exact():
     """max_ctx only shapes the split plan: a request whose context exceeds it is still computed
     exactly (its last split is longer)."""
