@@ -109,6 +109,37 @@ def test_prefill_block_edges(d_head):
     _run_mixed(c, with_verify=False, tag=f"prefill block edges d{d_head}")
 
 
+@pytest.mark.parametrize("d_head,hq,hkv", [(64, 4, 2), (128, 8, 2), (256, 6, 2)])
+def test_prefill_single_row_closed_form(d_head, hq, hkv):
+    """A one-row prefill request with no context sees only its own key: probability exactly 1,
+    so its output is its value row (pool row kv_base + 0) bit for bit and lse = scale q.k;
+    the longer requests beside it are checked against the oracle."""
+    c = _prefill_case(62 + d_head, q_len=[1, 40, 1], ctx=[0, 0, 0], hq=hq, hkv=hkv, d=d_head)
+    _run_mixed(c, with_verify=False, tag=f"prefill single row d{d_head}")
+    pf = c["prefill"]
+    d = device_case(c)
+    pf_q = to_dev(pf["q"])
+    pf_out = torch.full_like(pf_q, float("nan"))
+    pf_lse = torch.full((pf_q.shape[0], hq), float("nan"), device=DEV)
+    prefill = dsv.Prefill(q_start=to_dev(pf["q_start"]), q_len=to_dev(pf["q_len"]),
+                          ctx_len=to_dev(pf["ctx_len"]), kv_base=to_dev(pf["kv_base"]), q=pf_q,
+                          out=pf_out, max_len=pf["max_len"], lse=pf_lse)
+    dsv.verify_attn(None, d["k_pool"], d["v_pool"], None, None, d["ctx_len"], d["kv_base"], W=16,
+                    max_ctx=0, status=d["status"], prefill=prefill)
+    torch.cuda.synchronize()
+    assert int(d["status"].item()) == 0
+    G = hq // hkv
+    q = to_f64(pf_q)
+    kp = to_f64(d["k_pool"])
+    for r in (0, 2):
+        row, base = int(pf["q_start"][r]), int(pf["kv_base"][r])
+        for h in range(hq):
+            g = h // G
+            assert torch.equal(pf_out[row, h].view(torch.int16), d["v_pool"][g, base].view(torch.int16)), (r, h)
+            z = float(q[row, h] @ kp[g, base]) / np.sqrt(d_head)
+            assert abs(float(pf_lse[row, h]) - z) <= 1e-3, (r, h, float(pf_lse[row, h]), z)
+
+
 def test_prefill_fp32():
     c = _prefill_case(57, q_len=[70, 5], ctx=[0, 33], hq=4, hkv=2, d=64, dtype="f32")
     _run_mixed(c, with_verify=False, tag="prefill fp32")
