@@ -42,7 +42,7 @@ PROFILED_KERNEL = "attn_bf16_kernel<128, 8, false, 64, 2, false>"
 # WRITE_SIZE runs (profiles/attn_verify_cfg3_hbm_traffic.md, calibrated there against the
 # streaming-read probe and a pool copy), valid for the kernel source with this SHA-256 only.
 COUNTED_SOURCE = ("block_verification_attention_amd/csrc/dsv_attn.hip",
-                  "7f5d2563aed18812550fa9ad46116ba3eb4433a025e63ef0090834ad016d26e1")
+                  "d46a5874595f3c69a6b32c548542bac483b5a43aafb7e2fbb00c9afe685782da")
 COUNTED_READ_BYTES = 270_444_171
 COUNTED_WRITE_BYTES = 5_523_292
 
@@ -260,29 +260,32 @@ def time_features(dev, copies: int = 2, iters: int = 10):
     return res
 
 
-def time_prefill(dev, iters: int = 20):
-    """Prefill attention with the 128-row wide tile (row a6; bf16 MFMA-bound) on the mixed
-    workload's prefill set: 4 fresh requests of 4096 causal rows (context 0), 32 query / 8 KV
-    heads, head_dim 128, seeded N(0,1) * 0.5 inputs made on the device.  Work per call:
-    sum over rows of the visible keys x 32 heads x 128 x 4 flop (Q.K and P.V) = 5.50e11
-    flop.  Device time per call from HIP events around each dsv_verify_attn call (prefill
-    only, the pool already holding the rows' K/V), median of `iters`, against the dense bf16
-    MFMA peak of 2.5 PFLOP/s."""
+def time_prefill(dev, iters: int = 20, lens=(4096,) * 4, hq: int = 32, hkv: int = 8, seed: int = 5005):
+    """Prefill attention with the 128-row wide tile (bf16 MFMA-bound).  Default: the
+    mixed workload's prefill set, 4 fresh requests of 4096 causal rows (context 0), 32 query /
+    8 KV heads, head_dim 128, seeded N(0,1) * 0.5 inputs made on the device.  Work per call:
+    sum over rows of the visible keys x query heads x 128 x 4 flop (Q.K and P.V): 5.50e11 flop
+    for the default set.  Device time per call from HIP events around each dsv_verify_attn call
+    (prefill only, the pool already holding the rows' K/V), median of `iters`, against the
+    dense bf16 MFMA peak of 2.5 PFLOP/s.  `lens`, `hq` and `hkv` give other sets (ragged
+    lengths, fewer KV heads)."""
     import numpy as np
     import torch
     import block_verification_attention_amd as dsv
-    n_req, q_len, hq, hkv, d = 4, 4096, 32, 8, 128
+    d = 128
+    lens = [int(x) for x in lens]
+    n_req = len(lens)
     g = torch.Generator(device=dev)
-    g.manual_seed(5005)
-    rows = n_req * q_len
+    g.manual_seed(seed)
+    rows = sum(lens)
+    starts = np.cumsum([0] + lens[:-1]).tolist()
     kp = (torch.randn((hkv, rows, d), generator=g, device=dev) * 0.5).to(torch.bfloat16)
     vp = (torch.randn((hkv, rows, d), generator=g, device=dev) * 0.5).to(torch.bfloat16)
     q = (torch.randn((rows, hq, d), generator=g, device=dev) * 0.5).to(torch.bfloat16)
     i32 = lambda a: torch.tensor(a, dtype=torch.int32, device=dev)  # noqa: E731
-    pf = dsv.Prefill(q_start=i32([r * q_len for r in range(n_req)]), q_len=i32([q_len] * n_req),
-                     ctx_len=i32([0] * n_req),
-                     kv_base=torch.tensor([r * q_len for r in range(n_req)], dtype=torch.int64, device=dev),
-                     q=q, out=torch.empty_like(q), max_len=q_len,
+    pf = dsv.Prefill(q_start=i32(starts), q_len=i32(lens), ctx_len=i32([0] * n_req),
+                     kv_base=torch.tensor(starts, dtype=torch.int64, device=dev),
+                     q=q, out=torch.empty_like(q), max_len=max(lens),
                      lse=torch.empty((rows, hq), dtype=torch.float32, device=dev))
     st = dsv.new_status(dev)
     args = dsv.attn_args(None, kp, vp, None, None, None, None, W=16, max_ctx=0, out=None, status=st,
@@ -298,9 +301,11 @@ def time_prefill(dev, iters: int = 20):
         evs.append((a, b))
     torch.cuda.synchronize()
     us = float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3
-    flop = 4.0 * hq * d * n_req * q_len * (q_len + 1) / 2
+    flop = sum(4.0 * hq * d * n * (n + 1) / 2 for n in lens)
     tflops = flop / (us * 1e-6) / 1e12
-    return {"workload": "prefill, 4 x 4096 causal rows, 32/8 heads, head_dim 128, bf16",
+    shape = (f"{n_req} x {lens[0]}" if len(set(lens)) == 1
+             else "lengths " + ", ".join(str(n) for n in lens))
+    return {"workload": f"prefill, {shape} causal rows, {hq}/{hkv} heads, head_dim 128, bf16",
             "kernel": "attn_bf16_kernel<128, 8, true, 32, 1, false>", "us": us, "flop": flop,
             "TFLOPs": tflops, "peak_TFLOPs": 2500.0, "frac": tflops / 2500.0,
             "status": int(st.item())}
@@ -847,6 +852,9 @@ def main():
     res["sampling"] = time_sampling(dev, args.copies)
     res["features"] = time_features(dev)
     res["prefill"] = time_prefill(dev)
+    # ragged lengths with 2 KV heads (8 query heads each): the row blocks of a request are
+    # spread over the XCDs by the launch's block order
+    res["prefill_ragged"] = time_prefill(dev, lens=(4096, 1024, 1024, 1024), hq=16, hkv=2, seed=5006)
     res["other_verify"] = time_other_verify(dev, ev)
     res["mixed_launch"] = time_mixed(dev)
     if args.cpu_sample > 0:

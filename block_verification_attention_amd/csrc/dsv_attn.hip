@@ -408,20 +408,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
   } else {
     // The G query heads of a (request, KV head, row block) read the same KV tiles: with
     // xcd_sib_pf they are consecutive blocks on one XCD (grid a multiple of 8 G).
+    // Block i runs on XCD i % 8.  With fewer than 8 heads per request in the order below and
+    // a multiple of 8 units per row block, every row block of a request would land on the same
+    // XCDs, so ragged lengths would load a few XCDs only: then request r of row block j is
+    // taken by the slot of request (r - j) mod n_pf, which walks each request over the XCDs.
     int bid = blockIdx.x, b, r;
     if (p.xcd_sib_pf) {
       const int slot = bid / kXcds;
       const int hig = slot % p.G;
       const int u = (slot / p.G) * kXcds + bid % kXcds;  // (row block, request, KV head)
-      const int per_u = p.n_pf * p.hkv;
-      b = p.pf_blocks - 1 - u / per_u;  // longest row blocks first
+      const int per_u = p.n_pf * p.hkv, j = u / per_u;
+      b = p.pf_blocks - 1 - j;  // longest row blocks first
       r = (u % per_u) / p.hkv;
+      if (p.hkv < kXcds) r = (r + j) % p.n_pf;
       g = u % p.hkv;
       h = g * p.G + hig;
     } else {
-      const int per = p.n_pf * p.hq;
-      b = p.pf_blocks - 1 - bid / per;  // longest row blocks first
+      const int per = p.n_pf * p.hq, j = bid / per;
+      b = p.pf_blocks - 1 - j;  // longest row blocks first
       r = (bid % per) / p.hq;
+      if (p.hq < kXcds) r = (r + j) % p.n_pf;
       h = (bid % per) % p.hq;
       g = h / p.G;
     }

@@ -90,6 +90,17 @@ def test_prefill_ragged(d_head, hq, hkv):
     _run_mixed(c, with_verify=False, tag=f"prefill d{d_head}")
 
 
+@pytest.mark.parametrize("d_head,hq,hkv,q_len,ctx", [
+    (128, 8, 2, [1100, 300, 600, 17], [0, 20, 0, 5]),   # KV-head grouped order, 5 row blocks
+    (64, 4, 4, [700, 130, 1, 260], [3, 0, 0, 40]),      # plain order (one query head per KV head), 6
+])
+def test_prefill_rotation_wraps(d_head, hq, hkv, q_len, ctx):
+    """More row blocks than requests with fewer than 8 heads per request, so the per-row-block
+    turn of requests over the XCDs wraps round: every row still comes out once and right."""
+    c = _prefill_case(63 + d_head, q_len=q_len, ctx=ctx, hq=hq, hkv=hkv, d=d_head)
+    _run_mixed(c, with_verify=False, tag=f"prefill rotation d{d_head}")
+
+
 # Query lengths and contexts around each head_dim's tile edges, so that rows end inside a
 # wave, a wave's tile or a workgroup's row block, and contexts start the diagonal mid-tile:
 # head_dim 128 runs 256-row workgroups of 8 waves x 32 rows on 32-row KV tiles; head_dim 64
