@@ -1403,9 +1403,11 @@ template <int D>
 static int launch_verify_g(const AttnParams &p, int grid, hipStream_t s, hipEvent_t e0,
                            hipEvent_t e1) {
   if constexpr (D >= 256) {
-    // wide heads: groups of 3 heads (G = 3, 5, 6, 9) run padded to 4 waves; groups of one
-    // or two heads are refused by the host checks
+    // wide heads: groups of one to four heads run on 4 waves (with fewer than 64 (head, row)
+    // pairs the waves past the last pair hold no heads and only move tile loads)
     switch (p.GW) {
+      case 1:
+      case 2:
       case 3:
       case 4: return launch_attn<D, 4, false>(p, grid, s, e0, e1);
       default: return -1;
@@ -1502,11 +1504,6 @@ static dsv_status verify_attn_impl(const dsv_attn_args *a, const dsv::PackOut *p
   if (a->hq < 1 || a->hkv < 1 || a->hq % a->hkv) return DSV_ERR_INVALID_ARG;
   const int G = a->hq / a->hkv;
   if (a->dtype == DSV_BF16 && G > 16) return DSV_ERR_UNSUPPORTED;
-  // bf16 verification at head_dim 256 with one or two query heads per KV head is switched
-  // off: a GPU memory fault was once seen for one query head per KV head on an earlier
-  // kernel schedule and its cause was never shown, so these groupings are refused rather
-  // than run on a kernel with no parity evidence for them
-  if (a->dtype == DSV_BF16 && a->d == 256 && G <= 2 && a->n_bs > 0) return DSV_ERR_UNSUPPORTED;
   if (!a->k_pool || !a->v_pool || a->pool_rows < 0 || a->stride_row < a->d || a->stride_head < 0)
     return DSV_ERR_INVALID_ARG;
   const int64_t salign = a->dtype == DSV_BF16 ? 8 : 4;

@@ -180,9 +180,7 @@ dsv_status dsv_allocate_pack(int32_t n_live, int32_t n_bs, int32_t W, int32_t m_
 /*   [offsets[n_bs], m_bs) are zero-filled (lse -inf); any other row is not   */
 /*   touched.  The pool is written only at the candidate (and pf_k_new) rows. */
 /* Supported: d in {64, 128, 256}; hq % hkv == 0; hq / hkv <= 16 (bf16);     */
-/*   W <= DSV_MAX_W.  A bf16 verification set with d = 256 needs             */
-/*   hq / hkv >= 3: one or two query heads per KV head at that head_dim are  */
-/*   refused with DSV_ERR_UNSUPPORTED (no parity evidence for those kernels). */
+/*   W <= DSV_MAX_W.                                                         */
 /* Errors (device): invalid request (k_i outside [0, W], negative ctx/base,  */
 /*   offsets[i] + k_i > m_bs, segment past pool_rows):                      */
 /*   DSV_STATUS_BAD_REQUEST or DSV_STATUS_POOL, its rows are zero-filled     */

@@ -56,17 +56,15 @@ def test_host_validation_without_gpu():
     assert lib.dsv_verify_attn(ctypes.byref(a), None) == 2
     a.hq, a.hkv = 3, 2
     assert lib.dsv_verify_attn(ctypes.byref(a), None) == 1
-    # bf16 verification at head_dim 256 with one or two query heads per KV head is refused
-    # (also through the fused packer); three heads pass this check and fail a later one (no
-    # pools); fp32 and a prefill-only call at that grouping are not refused by it
+    # bf16 verification at head_dim 256 takes every grouping of one to sixteen query heads per
+    # KV head (also through the fused packer): these pass the grouping checks and fail a later
+    # one (no pools)
     a.d, a.n_bs, a.m_bs, a.W = 256, 2, 8, 16
-    for hq, hkv in ((4, 4), (2, 1), (8, 4)):
+    for hq, hkv in ((4, 4), (2, 1), (8, 4), (6, 2), (16, 1)):
         a.hq, a.hkv = hq, hkv
-        assert lib.dsv_verify_attn(ctypes.byref(a), None) == 2, (hq, hkv)
+        assert lib.dsv_verify_attn(ctypes.byref(a), None) == 1, (hq, hkv)
         dmy = ctypes.c_void_p(16)
-        assert lib.dsv_pack_verify_attn(ctypes.byref(a), dmy, dmy, dmy, dmy, dmy, dmy, None) == 2
-    a.hq, a.hkv = 6, 2
-    assert lib.dsv_verify_attn(ctypes.byref(a), None) == 1
+        assert lib.dsv_pack_verify_attn(ctypes.byref(a), dmy, dmy, dmy, dmy, dmy, dmy, None) == 1
     a.hq, a.hkv, a.dtype = 4, 4, 1
     assert lib.dsv_verify_attn(ctypes.byref(a), None) == 1
     a.dtype, a.n_bs = 0, 0

@@ -35,14 +35,12 @@ def test_config1_fp32():
                                             # groups split unevenly over workgroups (the last
                                             # one holds fewer heads) or padded to a wider one
                                             (128, 9, 1), (128, 11, 1), (256, 5, 1), (256, 7, 1),
-                                            (256, 10, 1), (256, 13, 1), (128, 2, 1), (128, 6, 1)])
+                                            (256, 10, 1), (256, 13, 1), (128, 2, 1), (128, 6, 1),
+                                            # head_dim 256 with one or two query heads per KV
+                                            # head (waves without heads in the 4-wave kernel)
+                                            (256, 2, 1), (256, 8, 4)])
 @pytest.mark.parametrize("kv_chunk", [0, 64, 256])
 def test_bf16_ragged(d_head, hq, hkv, kv_chunk):
-    if (d_head, hq, hkv) == (256, 4, 4):
-        pytest.skip("head_dim 256 with one query head per KV head: a GPU memory fault was seen "
-                    "with an earlier schedule of direct global->LDS loads for this shape (that "
-                    "code is gone); its cause was never shown, so the case stays off the GPU and "
-                    "the library refuses the grouping (DSV_ERR_UNSUPPORTED, checked on the CPU)")
     c = small_case(10 + d_head + hq, hq=hq, hkv=hkv, d=d_head,
                    k=(16, 5, 0, 11, 1, 16, 3), ctx=(700, 0, 40, 63, 64, 1000, 129))
     _run(c, kv_chunk=kv_chunk, tag=f"d{d_head} hq{hq} hkv{hkv} chunk{kv_chunk}")
@@ -180,7 +178,7 @@ def test_invalid_requests_flagged_and_zeroed():
     assert torch.isnan(out[off[2]:off[2] + 3].float()).all()
 
 
-@pytest.mark.parametrize("d_head,hq,hkv", [(64, 4, 2), (128, 8, 2), (256, 6, 2)])
+@pytest.mark.parametrize("d_head,hq,hkv", [(64, 4, 2), (128, 8, 2), (256, 6, 2), (256, 2, 2)])
 def test_zero_context_requests(d_head, hq, hkv):
     """Requests with no committed context.  A single anchor (k_i = 1, ctx_i = 0) sees only
     itself: its probability is exactly 1, so its output is its own value row bit for bit and
