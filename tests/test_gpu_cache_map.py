@@ -58,7 +58,7 @@ def run_mapped(c, d, packed, kp, vp, idx, *, use_new=True, kv_chunk=0, loc_idx=N
 
 
 @pytest.mark.parametrize("dtype,d_head,hq,hkv", [("bf16", 128, 32, 8), ("bf16", 64, 8, 2), ("bf16", 128, 12, 4),
-                                                 ("bf16", 256, 24, 2), ("f32", 64, 4, 2)])
+                                                 ("bf16", 256, 24, 2), ("bf16", 256, 2, 2), ("f32", 64, 4, 2)])
 @pytest.mark.parametrize("use_new", [True, False])
 def test_cache_map_parity(dtype, d_head, hq, hkv, use_new):
     c = small_case(40 + d_head + hq, dtype=dtype, hq=hq, hkv=hkv, d=d_head,
