@@ -63,7 +63,7 @@ def test_config3_full():
     _check_against_composed_and_oracle(wl.config3(with_logits=False), tag="cfg3")
 
 
-@pytest.mark.parametrize("d_head,hq,hkv", [(128, 32, 8), (64, 16, 2), (256, 24, 2), (128, 13, 1)])
+@pytest.mark.parametrize("d_head,hq,hkv", [(128, 32, 8), (64, 16, 2), (256, 24, 2), (128, 13, 1), (256, 4, 4)])
 @pytest.mark.parametrize("kv_chunk", [0, 64])
 def test_ragged(d_head, hq, hkv, kv_chunk):
     c = small_case(300 + d_head + hq, hq=hq, hkv=hkv, d=d_head,
