@@ -382,7 +382,8 @@ def time_other_verify(dev, ev, iters: int = 20):
     with their seeded prefix lengths and contexts and seeded N(0,1) * 0.5 device-made K/V:
     32 requests sharing 256 slots at contexts U[4096, 8192], 24 query / 2 KV heads, head_dim
     256 (12 query heads per KV head); and 60 requests sharing 480 slots at contexts
-    U[8192, 32768], 32 / 8 heads, head_dim 128.  Kernel time from the start/stop events
+    U[8192, 32768], 32 / 8 heads, head_dim 128.  Also the first shape's requests with 8 query
+    heads on 8 KV heads (one per KV head, head_dim 256).  Kernel time from the start/stop events
     attached to the verification kernel's launch (median of `iters`), algorithmic KV bytes
     (every visible K and V row once) over it, against 8 TB/s."""
     import numpy as np
@@ -393,6 +394,7 @@ def time_other_verify(dev, ev, iters: int = 20):
     shapes = {
         "32x256_slots_ctx4k-8k_24q2kv_d256": (4, 32, 256, 4096, 8193, 24, 2, 256, 2),
         "60x480_slots_ctx8k-32k_32q8kv_d128": (5, 60, 480, 8192, 32769, 32, 8, 128, 1),
+        "32x256_slots_ctx4k-8k_8q8kv_d256": (4, 32, 256, 4096, 8193, 8, 8, 256, 1),
     }
     for name, (cfg, n, m_bs, lo, hi, hq, hkv, d, copies) in shapes.items():
         g = wl.rng(cfg, 0)
