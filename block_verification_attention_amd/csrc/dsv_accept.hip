@@ -391,6 +391,18 @@ extern "C" dsv_status dsv_accept(int32_t n_bs, int32_t m_bs, int32_t W, int32_t 
   const size_t need = dsv_accept_workspace_bytes(tgt ? m_bs : 0, tgt ? vocab : 0, drf ? n_bs : 0,
                                                  drf ? n_pos : 0, drf ? draft_vocab : 0);
   if (need > 0 && (!workspace || workspace_bytes < need)) return DSV_ERR_WORKSPACE;
+  {
+    const int64_t mt = tgt ? m_bs : 0, nt = tgt ? n_bs : 0, nd = drf ? (int64_t)n_bs * n_pos : 0;
+    const Span out[] = {{slot_argmax, span_bytes(mt, 4)}, {accepted, span_bytes(nt, 4)},
+                        {bonus, span_bytes(nt, 4)},       {progress, span_bytes(nt, 4)},
+                        {out_tokens, span_bytes(nt * W, 4)}, {margin, span_bytes(nd, 4)},
+                        {draft_top1, span_bytes(nd, 4)},  {workspace, need},
+                        {status, 4}};
+    const Span in[] = {{target_logits, span_bytes(mt * vocab, 4)}, {slot_tok, span_bytes(mt, 4)},
+                       {offsets, span_bytes(nt + (tgt ? 1 : 0), 4)}, {k, span_bytes(nt, 4)},
+                       {draft_logits, span_bytes(nd * (drf ? draft_vocab : 0), 4)}};
+    if (outputs_alias(out, in)) return DSV_ERR_INVALID_ARG;
+  }
 
   char *ws = static_cast<char *>(workspace);
   uint64_t *keys = nullptr;

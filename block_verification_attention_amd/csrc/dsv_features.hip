@@ -324,6 +324,11 @@ extern "C" dsv_status dsv_draft_features(int64_t rows, int32_t vocab, const floa
   if (!draft_logits || !features) return DSV_ERR_INVALID_ARG;
   const size_t need = dsv_draft_features_workspace_bytes(rows, vocab);
   if (!workspace || workspace_bytes < need) return DSV_ERR_WORKSPACE;
+  {
+    const Span out[] = {{features, span_bytes(rows * kFeat, 4)}, {workspace, need}, {status, 4}};
+    const Span in[] = {{draft_logits, span_bytes(rows * vocab, 4)}};
+    if (outputs_alias(out, in)) return DSV_ERR_INVALID_ARG;
+  }
   int nc, ch;
   plan_feat(rows, vocab, &nc, &ch);
   if (rows * nc >= ((int64_t)1 << 31)) return DSV_ERR_INVALID_ARG;

@@ -145,3 +145,40 @@ __device__ __forceinline__ void write_request_slots(int i, int k, int off, int W
   do {                                                  \
     if (hipGetLastError() != hipSuccess) return DSV_ERR_HIP; \
   } while (0)
+
+namespace dsv {
+// Host-side aliasing check.  A Span is the byte range [p, p + bytes) an argument covers (a
+// null p or zero bytes cover nothing).
+struct Span {
+  const void *p;
+  size_t bytes;
+};
+inline bool spans_overlap(const Span &a, const Span &b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t x = (uintptr_t)a.p, y = (uintptr_t)b.p;
+  return x >= y ? x - y < b.bytes : y - x < a.bytes;
+}
+// Bytes of n elements of elem bytes (none for n <= 0).
+inline size_t span_bytes(int64_t n, size_t elem) { return n > 0 ? (size_t)n * elem : 0; }
+// True when an output shares a byte with another output or with an input, or a read-write
+// buffer (shared) with an output or an input.  Inputs may share bytes with each other, and
+// read-write buffers with each other (two views of one allocation, such as K and V pools
+// interleaved by head).
+template <size_t NO, size_t NI, size_t NS = 1>
+inline bool outputs_alias(const Span (&out)[NO], const Span (&in)[NI],
+                          const Span (&shared)[NS] = {{nullptr, 0}}) {
+  for (size_t i = 0; i < NO; ++i) {
+    for (size_t j = i + 1; j < NO; ++j)
+      if (spans_overlap(out[i], out[j])) return true;
+    for (size_t j = 0; j < NI; ++j)
+      if (spans_overlap(out[i], in[j])) return true;
+  }
+  for (size_t s = 0; s < NS; ++s) {
+    for (size_t i = 0; i < NO; ++i)
+      if (spans_overlap(shared[s], out[i])) return true;
+    for (size_t j = 0; j < NI; ++j)
+      if (spans_overlap(shared[s], in[j])) return true;
+  }
+  return false;
+}
+}  // namespace dsv

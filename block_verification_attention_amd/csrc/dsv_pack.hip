@@ -257,6 +257,16 @@ extern "C" dsv_status dsv_pack_slots(int32_t n_bs, int32_t W, int32_t m_bs, cons
   if (!offsets || !status) return DSV_ERR_INVALID_ARG;
   if (n_bs > 0 && (!k || !ctx_len || !kv_base || !block_tokens)) return DSV_ERR_INVALID_ARG;
   if (m_bs > 0 && (!slot_req || !slot_tok || !slot_pos || !slot_cache_loc)) return DSV_ERR_INVALID_ARG;
+  {
+    using dsv::span_bytes;
+    const dsv::Span out[] = {{offsets, span_bytes(n_bs + 1, 4)}, {slot_req, span_bytes(m_bs, 4)},
+                             {slot_tok, span_bytes(m_bs, 4)},    {slot_pos, span_bytes(m_bs, 4)},
+                             {slot_cache_loc, span_bytes(m_bs, 8)}, {status, 4}};
+    const dsv::Span in[] = {{k, span_bytes(n_bs, 4)}, {ctx_len, span_bytes(n_bs, 4)},
+                            {kv_base, span_bytes(n_bs, 8)},
+                            {block_tokens, span_bytes((int64_t)n_bs * W, 4)}};
+    if (dsv::outputs_alias(out, in)) return DSV_ERR_INVALID_ARG;
+  }
   // enough threads for one request each (or for the tail fill), up to one 1024-thread block
   int64_t want = n_bs > m_bs ? n_bs : m_bs;
   if (want < 64) want = 64;
@@ -281,6 +291,17 @@ extern "C" dsv_status dsv_allocate_pack(int32_t n_live, int32_t n_bs, int32_t W,
   if (n_live > 0 && W > 1 && !scores) return DSV_ERR_INVALID_ARG;
   if (n_bs > 0 && (!ctx_len || !kv_base || !block_tokens)) return DSV_ERR_INVALID_ARG;
   if (m_bs > 0 && (!slot_req || !slot_tok || !slot_pos || !slot_cache_loc)) return DSV_ERR_INVALID_ARG;
+  {
+    using dsv::span_bytes;
+    const dsv::Span out[] = {{k, span_bytes(n_bs, 4)},           {k0, span_bytes(n_bs, 4)},
+                             {offsets, span_bytes(n_bs + 1, 4)}, {slot_req, span_bytes(m_bs, 4)},
+                             {slot_tok, span_bytes(m_bs, 4)},    {slot_pos, span_bytes(m_bs, 4)},
+                             {slot_cache_loc, span_bytes(m_bs, 8)}, {status, 4}};
+    const dsv::Span in[] = {{scores, span_bytes((int64_t)n_live * (W - 1), 4)},
+                            {ctx_len, span_bytes(n_bs, 4)}, {kv_base, span_bytes(n_bs, 8)},
+                            {block_tokens, span_bytes((int64_t)n_bs * W, 4)}};
+    if (dsv::outputs_alias(out, in)) return DSV_ERR_INVALID_ARG;
+  }
   int want = n_bs > 64 ? n_bs : 64;
   const int nt = (want + 63) / 64 * 64;
   hipLaunchKernelGGL(dsv::allocate_pack_kernel, dim3(1), dim3(nt), 0, stream, n_live, n_bs, W, m_live,

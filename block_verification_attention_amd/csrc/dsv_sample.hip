@@ -440,6 +440,17 @@ extern "C" dsv_status dsv_accept_sample(int32_t n_bs, int32_t m_bs, int32_t W, i
   if (n_bs == 0) return DSV_OK;
   const size_t need = dsv_accept_sample_workspace_bytes(n_bs, m_bs > 0 ? m_bs : 1, vocab);
   if (!workspace || workspace_bytes < need) return DSV_ERR_WORKSPACE;
+  {
+    const Span out[] = {{accepted, span_bytes(n_bs, 4)},  {bonus, span_bytes(n_bs, 4)},
+                        {progress, span_bytes(n_bs, 4)},  {out_tokens, span_bytes((int64_t)n_bs * W, 4)},
+                        {p_cand, span_bytes(m_bs, 4)},    {workspace, need},
+                        {status, 4}};
+    const Span in[] = {{target_logits, span_bytes((int64_t)m_bs * vocab, 4)},
+                       {slot_tok, span_bytes(m_bs, 4)}, {offsets, span_bytes(n_bs + 1, 4)},
+                       {k, span_bytes(n_bs, 4)},        {u_accept, span_bytes(m_bs, 4)},
+                       {u_draw, span_bytes(n_bs, 4)}};
+    if (outputs_alias(out, in)) return DSV_ERR_INVALID_ARG;
+  }
   int nc1, ch1, nc2, ch2;
   plan_stats(m_bs > 0 ? m_bs : 1, vocab, &nc1, &ch1);
   plan_draw(n_bs, vocab, &nc2, &ch2);

@@ -25,7 +25,12 @@
  *   host readback for slice reconstruction).
  * - Host-detectable errors (null required pointer, sizes out of range,
  *   unsupported head configuration, workspace too small) return a non-zero
- *   dsv_status before anything is enqueued.
+ *   dsv_status before anything is enqueued.  So does aliasing: an output
+ *   (the status word and the workspace included) that shares a byte with
+ *   another output or with an input, over the extents the call's sizes give,
+ *   is refused with DSV_ERR_INVALID_ARG.  Inputs may share bytes; the KV
+ *   pools, read and written, may share an allocation with each other (for
+ *   example K and V interleaved by head) but with no other argument.
  * - Data-dependent errors are reported in the caller's device word `status`
  *   (int32, OR-ed with the DSV_STATUS_* bits below; the library never clears
  *   it) and the affected outputs take the defined values stated per call.
@@ -46,7 +51,7 @@ extern "C" {
 
 typedef enum dsv_status {
   DSV_OK = 0,
-  DSV_ERR_INVALID_ARG = 1, /* null required pointer, size or layout out of range */
+  DSV_ERR_INVALID_ARG = 1, /* null required pointer, size or layout out of range, aliasing */
   DSV_ERR_UNSUPPORTED = 2, /* head_dim / grouping / dtype the kernels do not cover */
   DSV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the query reports */
   DSV_ERR_HIP = 4          /* a HIP launch failed */

@@ -141,6 +141,81 @@ def test_host_validation_next_rows_without_gpu():
     assert st.value == 0
 
 
+def test_aliasing_refused_without_gpu():
+    """An output that shares a byte with another output or with an input is refused with
+    DSV_ERR_INVALID_ARG before anything is enqueued (fake, 256-byte aligned, far-apart device
+    addresses; each call has exactly one overlap)."""
+    lib = _lib.load()
+    st = ctypes.c_int32(0)
+    sp = ctypes.addressof(st)
+    base = 1 << 40
+    slot = iter(range(1, 1000))
+    fresh = lambda: base + next(slot) * (1 << 32)  # noqa: E731
+    P = ctypes.c_void_p
+    # pack: offsets[1] is k[0]; slot_pos is slot_tok shifted by 4 bytes
+    k, ctx, kvb, tok = fresh(), fresh(), fresh(), fresh()
+    outs = [fresh() for _ in range(5)]
+    assert lib.dsv_pack_slots(4, 16, 64, P(k), P(ctx), P(kvb), P(tok), P(k - 4), P(outs[1]), P(outs[2]),
+                              P(outs[3]), P(outs[4]), sp, None) == 1
+    assert lib.dsv_pack_slots(4, 16, 64, P(k), P(ctx), P(kvb), P(tok), P(outs[0]), P(outs[1]),
+                              P(outs[2]), P(outs[2] + 4), P(outs[4]), sp, None) == 1
+    # the status word inside an output
+    assert lib.dsv_pack_slots(4, 16, 64, P(k), P(ctx), P(kvb), P(tok), P(outs[0]), P(outs[1]),
+                              P(outs[2]), P(outs[3]), P(outs[4]), P(outs[1] + 8), None) == 1
+    # allocator: the adjusted lengths over the last score row
+    sc = fresh()
+    assert lib.dsv_allocate_pack(4, 8, 16, 32, 64, P(sc), P(ctx), P(kvb), P(tok), P(sc + 3 * 15 * 4),
+                                 None, P(outs[0]), P(outs[1]), P(outs[2]), P(outs[3]), P(outs[4]),
+                                 sp, None) == 1
+
+    def attn(**over):
+        a = _lib.AttnArgs()
+        a.dtype, a.hq, a.hkv, a.d, a.W, a.max_ctx = 0, 8, 2, 128, 16, 64
+        a.n_bs, a.m_bs = 2, 32
+        a.pool_rows, a.stride_row = 256, 128
+        a.stride_head = 256 * 128
+        for name in ("k_pool", "v_pool", "offsets", "k", "ctx_len", "kv_base", "slot_cache_loc",
+                     "q", "k_new", "v_new", "out", "lse"):
+            setattr(a, name, fresh())
+        a.status = sp
+        for name, v in over.items():
+            setattr(a, name, v(a) if callable(v) else v)
+        return a
+
+    # verification: out over q, lse inside out, out over a pool, q over a pool (pools are read
+    # and written), a pool over the status word
+    for over in ({"out": lambda a: a.q}, {"lse": lambda a: a.out + 1024},
+                 {"out": lambda a: a.k_pool + 2 * 256 * 128}, {"q": lambda a: a.v_pool},
+                 {"status": lambda a: a.k_pool + 64}):
+        a = attn(**over)
+        assert lib.dsv_verify_attn(ctypes.byref(a), None) == 1, over
+        assert lib.dsv_verify_attn_noalloc(ctypes.byref(a), None) == 1, over
+    # fused packer: a packer output over the request lengths
+    a = attn(offsets=None)
+    bt = fresh()
+    assert lib.dsv_pack_verify_attn(ctypes.byref(a), P(bt), P(fresh()), P(a.k), P(fresh()),
+                                    P(fresh()), P(fresh()), None) == 1
+    # accept: the argmax output over the logits; the workspace over the draft tokens
+    need = lib.dsv_accept_workspace_bytes(64, 1000, 4, 15, 1000)
+    lg, stok, ws = fresh(), fresh(), fresh()
+    args = lambda sa, wsp: (4, 64, 16, 1000, P(lg), P(stok), P(fresh()), P(fresh()), P(sa),  # noqa: E731
+                            P(fresh()), P(fresh()), P(fresh()), P(fresh()), P(fresh()), 15, 1000,
+                            P(fresh()), P(fresh()), P(wsp), need, sp, None)
+    assert lib.dsv_accept(*args(lg + 4 * 1000 * 63, ws)) == 1
+    assert lib.dsv_accept(*args(fresh(), stok - 256)) == 1
+    # sampling verifier: p_cand over the acceptance uniforms
+    need = lib.dsv_accept_sample_workspace_bytes(4, 64, 1000)
+    ua = fresh()
+    assert lib.dsv_accept_sample(4, 64, 16, 1000, P(lg), 1.0, P(stok), P(fresh()), P(fresh()), P(ua),
+                                 P(fresh()), P(fresh()), P(fresh()), P(fresh()), P(fresh()), P(ua),
+                                 P(fresh()), need, sp, None) == 1
+    # draft features: the features over the logits
+    need = lib.dsv_draft_features_workspace_bytes(4, 4096)
+    dl = fresh()
+    assert lib.dsv_draft_features(4, 4096, P(dl), P(dl + 4096 * 4 * 3), P(fresh()), need, sp, None) == 1
+    assert st.value == 0
+
+
 def test_workspace_queries():
     lib = _lib.load()
     assert lib.dsv_accept_workspace_bytes(128, 151936, 0, 0, 0) > 0

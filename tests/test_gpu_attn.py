@@ -91,6 +91,31 @@ def test_candidate_kv_written_at_cache_refs():
     assert np.array_equal(bits_of(d["v_pool"]), ref_v)
 
 
+def test_pools_interleaved_by_head():
+    """K and V pools as two views of one allocation [hkv][2][rows][d]: interleaved by head,
+    their byte ranges overlap, which the aliasing check allows for the pools (they are
+    compared only with the other buffers).  Parity, and the candidate rows written into
+    their own view."""
+    c = small_case(44, hq=8, hkv=2, d=128, k=(16, 5, 0, 11), ctx=(300, 0, 40, 129))
+    d = device_case(c)
+    hkv, rows, dd = d["k_pool"].shape
+    buf = torch.empty((hkv, 2, rows, dd), dtype=d["k_pool"].dtype, device=DEV)
+    buf[:, 0] = d["k_pool"]
+    buf[:, 1] = d["v_pool"]
+    d["k_pool"], d["v_pool"] = buf[:, 0], buf[:, 1]
+    packed = gpu_pack(c, d)
+    ref_pack = oracle_pack(c)
+    out, lse = gpu_attn(c, d, packed)
+    torch.cuda.synchronize()
+    assert int(d["status"].item()) == 0
+    ref_out, ref_lse = oracle_attn(c, ref_pack["offsets"])
+    compare_attn(c, ref_pack["offsets"], out, lse, ref_out, ref_lse, tag="pools interleaved by head")
+    ref_k, ref_v = oracle.scatter_candidates(c["k_pool"], c["v_pool"], c["k_new"], c["v_new"],
+                                             ref_pack["slot_cache_loc"])
+    assert np.array_equal(bits_of(buf[:, 0]), ref_k)
+    assert np.array_equal(bits_of(buf[:, 1]), ref_v)
+
+
 def test_packed_equals_padded_and_deterministic():
     """Same requests launched packed and padded (each request owns W rows, gaps between
     them): valid rows are bit-identical with the split size pinned; two runs agree bitwise."""
