@@ -407,8 +407,12 @@ extern "C" dsv_status dsv_accept(int32_t n_bs, int32_t m_bs, int32_t W, int32_t 
   char *ws = static_cast<char *>(workspace);
   uint64_t *keys = nullptr;
   int nc_t = 1, ch_t = 0, nc_d = 1, ch_d = 0;
+  if (tgt && m_bs > 0) plan_chunks(m_bs, vocab, &nc_t, &ch_t);
+  if (drf) plan_chunks((int64_t)n_bs * n_pos, draft_vocab, &nc_d, &ch_d);
+  if (!launch_fits(tgt ? (int64_t)m_bs * nc_t : 0, kAccThreads) ||
+      !launch_fits(drf ? (int64_t)n_bs * n_pos * nc_d : 0, kAccThreads))
+    return DSV_ERR_INVALID_ARG;
   if (tgt && m_bs > 0) {
-    plan_chunks(m_bs, vocab, &nc_t, &ch_t);
     keys = reinterpret_cast<uint64_t *>(ws);
     ws += align256((size_t)m_bs * nc_t * sizeof(uint64_t));
     const bool vec = (vocab % 4 == 0) && ((uintptr_t)target_logits % 16 == 0);
@@ -426,7 +430,6 @@ extern "C" dsv_status dsv_accept(int32_t n_bs, int32_t m_bs, int32_t W, int32_t 
   Top2 *dpart = nullptr;
   if (drf) {
     const int64_t rows = (int64_t)n_bs * n_pos;
-    plan_chunks(rows, draft_vocab, &nc_d, &ch_d);
     dpart = reinterpret_cast<Top2 *>(ws);
     const bool vec = (draft_vocab % 4 == 0) && ((uintptr_t)draft_logits % 16 == 0);
     const int64_t grid = rows * nc_d;

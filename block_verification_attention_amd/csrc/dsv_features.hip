@@ -331,7 +331,7 @@ extern "C" dsv_status dsv_draft_features(int64_t rows, int32_t vocab, const floa
   }
   int nc, ch;
   plan_feat(rows, vocab, &nc, &ch);
-  if (rows * nc >= ((int64_t)1 << 31)) return DSV_ERR_INVALID_ARG;
+  if (!launch_fits(rows * nc, kFtThreads)) return DSV_ERR_INVALID_ARG;
   FeatPart *part = static_cast<FeatPart *>(workspace);
   const bool vec = (vocab % 4 == 0) && ((uintptr_t)draft_logits % 16 == 0);
   hipLaunchKernelGGL(feat_partial_kernel, dim3((unsigned)(rows * nc)), dim3(kFtThreads), 0, stream,

@@ -158,6 +158,11 @@ inline bool spans_overlap(const Span &a, const Span &b) {
   const uintptr_t x = (uintptr_t)a.p, y = (uintptr_t)b.p;
   return x >= y ? x - y < b.bytes : y - x < a.bytes;
 }
+// A 1-D launch of `blocks` workgroups of `threads` work-items: at most 2^32 - 1 work-items
+// (the dispatch's grid size is 32-bit) and a block index that fits an int.
+inline bool launch_fits(int64_t blocks, int64_t threads) {
+  return blocks >= 0 && blocks <= INT32_MAX && blocks * threads <= (int64_t)UINT32_MAX;
+}
 // Bytes of n elements of elem bytes (none for n <= 0).
 inline size_t span_bytes(int64_t n, size_t elem) { return n > 0 ? (size_t)n * elem : 0; }
 // True when an output shares a byte with another output or with an input, or a read-write

@@ -55,7 +55,7 @@ extern "C" dsv_status dsv_philox_uniforms(uint64_t key0, uint64_t key1, uint64_t
   if (n == 0) return DSV_OK;
   const int64_t blocks = (n + 3) / 4;
   const int64_t grid = (blocks + kRngThreads - 1) / kRngThreads;
-  if (grid > INT32_MAX) return DSV_ERR_INVALID_ARG;
+  if (!launch_fits(grid, kRngThreads)) return DSV_ERR_INVALID_ARG;
   hipLaunchKernelGGL(philox_uniforms_kernel, dim3((unsigned)grid), dim3(kRngThreads), 0, stream,
                      key0, key1, counter_lo, counter_hi, n, out);
   DSV_LAUNCH_CHECK();

@@ -454,6 +454,9 @@ extern "C" dsv_status dsv_accept_sample(int32_t n_bs, int32_t m_bs, int32_t W, i
   int nc1, ch1, nc2, ch2;
   plan_stats(m_bs > 0 ? m_bs : 1, vocab, &nc1, &ch1);
   plan_draw(n_bs, vocab, &nc2, &ch2);
+  if (!launch_fits((int64_t)(m_bs > 0 ? m_bs : 1) * nc1, kSmpThreads) ||
+      !launch_fits((int64_t)n_bs * nc2, kSmpThreads))
+    return DSV_ERR_INVALID_ARG;
   char *ws = static_cast<char *>(workspace);
   SoftStat *stats = reinterpret_cast<SoftStat *>(ws);
   ws += align256s((size_t)(m_bs > 0 ? m_bs : 1) * nc1 * sizeof(SoftStat));

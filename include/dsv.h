@@ -30,7 +30,9 @@
  *   another output or with an input, over the extents the call's sizes give,
  *   is refused with DSV_ERR_INVALID_ARG.  Inputs may share bytes; the KV
  *   pools, read and written, may share an allocation with each other (for
- *   example K and V interleaved by head) but with no other argument.
+ *   example K and V interleaved by head) but with no other argument.  Sizes
+ *   whose launches would exceed a dispatch's 2^32 - 1 work-items are refused
+ *   with DSV_ERR_INVALID_ARG as well (before the call's first launch).
  * - Data-dependent errors are reported in the caller's device word `status`
  *   (int32, OR-ed with the DSV_STATUS_* bits below; the library never clears
  *   it) and the affected outputs take the defined values stated per call.

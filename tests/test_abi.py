@@ -216,6 +216,52 @@ def test_aliasing_refused_without_gpu():
     assert st.value == 0
 
 
+def test_launch_limits_refused_without_gpu():
+    """A call whose launches would exceed a dispatch's 2^32 - 1 work-items is refused with
+    DSV_ERR_INVALID_ARG before anything is enqueued (fake, far-apart device addresses)."""
+    lib = _lib.load()
+    st = ctypes.c_int32(0)
+    sp = ctypes.addressof(st)
+    base = 1 << 40
+    slot = iter(range(1, 1000))
+    fresh = lambda: ctypes.c_void_p(base + next(slot) * (1 << 36))  # noqa: E731
+    # fp32 prefill: one 256-thread workgroup per (row, query head): 2^25 rows x 8 heads
+    a = _lib.AttnArgs()
+    a.dtype, a.hq, a.hkv, a.d, a.W = 1, 8, 8, 64, 16
+    a.pool_rows, a.stride_row, a.stride_head = 64, 64, 64 * 64
+    a.k_pool, a.v_pool = fresh().value, fresh().value
+    a.n_pf, a.pf_max_len, a.pf_q_rows = 1, 1 << 25, 16
+    for name in ("pf_q_start", "pf_q_len", "pf_ctx_len", "pf_kv_base", "pf_q", "pf_out"):
+        setattr(a, name, fresh().value)
+    a.status = sp
+    assert lib.dsv_verify_attn(ctypes.byref(a), None) == 1
+    # bf16 verification with 64-row splits over a context of 2^30 rows: 2^24 splits x 8
+    # KV heads x up to 1024 threads
+    b = _lib.AttnArgs()
+    b.dtype, b.hq, b.hkv, b.d, b.W, b.max_ctx, b.kv_chunk = 0, 32, 8, 128, 16, 1 << 30, 64
+    b.n_bs, b.m_bs = 1, 16
+    b.pool_rows, b.stride_row, b.stride_head = 1 << 20, 128, 128 << 20
+    for name in ("k_pool", "v_pool", "offsets", "k", "ctx_len", "kv_base", "slot_cache_loc", "q",
+                 "out"):
+        setattr(b, name, fresh().value)
+    b.status = sp
+    assert lib.dsv_verify_attn(ctypes.byref(b), None) == 1
+    # greedy accept and the sampling verifier over 2^24 + 1 rows of 16 logits
+    m = (1 << 24) + 1
+    need = lib.dsv_accept_workspace_bytes(m, 16, 0, 0, 0)
+    assert lib.dsv_accept(1, m, 16, 16, fresh(), fresh(), fresh(), fresh(), fresh(), fresh(), fresh(),
+                          fresh(), None, None, 0, 0, None, None, fresh(), need, sp, None) == 1
+    need = lib.dsv_accept_sample_workspace_bytes(1, m, 16)
+    assert lib.dsv_accept_sample(1, m, 16, 16, fresh(), 1.0, fresh(), fresh(), fresh(), fresh(),
+                                 fresh(), fresh(), fresh(), fresh(), None, None, fresh(), need, sp,
+                                 None) == 1
+    # draft features over 2^24 rows; uniforms: 2^40 values
+    need = lib.dsv_draft_features_workspace_bytes(1 << 24, 16)
+    assert lib.dsv_draft_features(1 << 24, 16, fresh(), fresh(), fresh(), need, sp, None) == 1
+    assert lib.dsv_philox_uniforms(1, 2, 0, 0, 1 << 40, fresh(), None) == 1
+    assert st.value == 0
+
+
 def test_workspace_queries():
     lib = _lib.load()
     assert lib.dsv_accept_workspace_bytes(128, 151936, 0, 0, 0) > 0
