@@ -1542,18 +1542,17 @@ static dsv_status verify_attn_impl(const dsv_attn_args *a, const dsv::PackOut *p
     const bool bf16 = a->dtype == DSV_BF16;
     bool fits = true;
     if (prefill) {
-      if (a->pf_k_new) fits = fits && launch_fits((int64_t)a->n_pf * a->pf_max_len * a->hkv, 256);
-      fits = fits && (bf16 ? launch_fits((int64_t)((a->pf_max_len + pf_rows(a->d) - 1) / pf_rows(a->d)) *
-                                             a->n_pf * a->hq, 64 * pf_waves(a->d))
-                           : launch_fits((int64_t)a->n_pf * a->pf_max_len * a->hq, 256));
+      if (a->pf_k_new) fits = fits && launch_fits(mul_sat({a->n_pf, a->pf_max_len, a->hkv}), 256);
+      fits = fits && (bf16 ? launch_fits(mul_sat({(a->pf_max_len + pf_rows(a->d) - 1) / pf_rows(a->d),
+                                                  a->n_pf, a->hq}), 64 * pf_waves(a->d))
+                           : launch_fits(mul_sat({a->n_pf, a->pf_max_len, a->hq}), 256));
     }
     if (verify) {
-      fits = fits && (bf16 ? launch_fits((int64_t)pl.n_splits * a->n_bs * a->hkv *
-                                             verify_head_groups(a->d, G), 16 * 64)
-                           : launch_fits((int64_t)a->n_bs * a->W * a->hq, 256));
+      fits = fits && (bf16 ? launch_fits(mul_sat({pl.n_splits, a->n_bs, a->hkv,
+                                                  verify_head_groups(a->d, G)}), 16 * 64)
+                           : launch_fits(mul_sat({a->n_bs, a->W, a->hq}), 256));
       if (bf16 && pl.n_splits > 1)
-        fits = fits && launch_fits(((int64_t)a->n_bs * a->W * a->hq + 256 / (a->d / 4) - 1) /
-                                       (256 / (a->d / 4)), 256);
+        fits = fits && launch_fits(mul_sat({a->n_bs, a->W, a->hq}) / (256 / (a->d / 4)) + 1, 256);
     }
     if (!fits) return DSV_ERR_INVALID_ARG;
   }

@@ -322,6 +322,9 @@ extern "C" dsv_status dsv_draft_features(int64_t rows, int32_t vocab, const floa
   if (rows < 0 || vocab < kTopK || !status) return DSV_ERR_INVALID_ARG;
   if (rows == 0) return DSV_OK;
   if (!draft_logits || !features) return DSV_ERR_INVALID_ARG;
+  int nc, ch;
+  plan_feat(rows, vocab, &nc, &ch);
+  if (!launch_fits(mul_sat({rows, nc}), kFtThreads)) return DSV_ERR_INVALID_ARG;
   const size_t need = dsv_draft_features_workspace_bytes(rows, vocab);
   if (!workspace || workspace_bytes < need) return DSV_ERR_WORKSPACE;
   {
@@ -329,9 +332,6 @@ extern "C" dsv_status dsv_draft_features(int64_t rows, int32_t vocab, const floa
     const Span in[] = {{draft_logits, span_bytes(rows * vocab, 4)}};
     if (outputs_alias(out, in)) return DSV_ERR_INVALID_ARG;
   }
-  int nc, ch;
-  plan_feat(rows, vocab, &nc, &ch);
-  if (!launch_fits(rows * nc, kFtThreads)) return DSV_ERR_INVALID_ARG;
   FeatPart *part = static_cast<FeatPart *>(workspace);
   const bool vec = (vocab % 4 == 0) && ((uintptr_t)draft_logits % 16 == 0);
   hipLaunchKernelGGL(feat_partial_kernel, dim3((unsigned)(rows * nc)), dim3(kFtThreads), 0, stream,

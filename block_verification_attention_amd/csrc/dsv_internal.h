@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "dsv.h"
 
 namespace dsv {
@@ -157,6 +159,16 @@ inline bool spans_overlap(const Span &a, const Span &b) {
   if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
   const uintptr_t x = (uintptr_t)a.p, y = (uintptr_t)b.p;
   return x >= y ? x - y < b.bytes : y - x < a.bytes;
+}
+// Product of non-negative counts, saturating at INT64_MAX (a negative factor gives -1).
+inline int64_t mul_sat(std::initializer_list<int64_t> xs) {
+  int64_t r = 1;
+  for (int64_t x : xs) {
+    if (x < 0) return -1;
+    if (x != 0 && r > INT64_MAX / x) return INT64_MAX;
+    r *= x;
+  }
+  return r;
 }
 // A 1-D launch of `blocks` workgroups of `threads` work-items: at most 2^32 - 1 work-items
 // (the dispatch's grid size is 32-bit) and a block index that fits an int.

@@ -259,6 +259,10 @@ def test_launch_limits_refused_without_gpu():
     need = lib.dsv_draft_features_workspace_bytes(1 << 24, 16)
     assert lib.dsv_draft_features(1 << 24, 16, fresh(), fresh(), fresh(), need, sp, None) == 1
     assert lib.dsv_philox_uniforms(1, 2, 0, 0, 1 << 40, fresh(), None) == 1
+    # absurd counts whose block products pass 64 bits are refused too (no wrap-around)
+    assert lib.dsv_draft_features(1 << 62, 16, fresh(), fresh(), fresh(), 1 << 20, sp, None) == 1
+    a.n_pf, a.pf_max_len, a.hq, a.hkv = (1 << 31) - 1, (1 << 31) - 1, 1 << 20, 1 << 20
+    assert lib.dsv_verify_attn(ctypes.byref(a), None) == 1
     assert st.value == 0
 
 
