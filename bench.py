@@ -42,7 +42,7 @@ PROFILED_KERNEL = "attn_bf16_kernel<128, 8, false, 64, 2, false>"
 # WRITE_SIZE runs (profiles/attn_verify_cfg3_hbm_traffic.md, calibrated there against the
 # streaming-read probe and a pool copy), valid for the kernel source with this SHA-256 only.
 COUNTED_SOURCE = ("block_verification_attention_amd/csrc/dsv_attn.hip",
-                  "b4e26f4507ea8adf701096d75e01b4dfb8bc74625a68fb8a4ca4325bfb0de5a5")
+                  "ea5b2e328d4b04abc4cab65542afe85410dc471e4e514f29e8aa26f3cbfcba40")
 COUNTED_READ_BYTES = 270_444_171
 COUNTED_WRITE_BYTES = 5_523_292
 

@@ -398,9 +398,9 @@ extern "C" dsv_status dsv_accept(int32_t n_bs, int32_t m_bs, int32_t W, int32_t 
                         {out_tokens, span_bytes(nt * W, 4)}, {margin, span_bytes(nd, 4)},
                         {draft_top1, span_bytes(nd, 4)},  {workspace, need},
                         {status, 4}};
-    const Span in[] = {{target_logits, span_bytes(mt * vocab, 4)}, {slot_tok, span_bytes(mt, 4)},
+    const Span in[] = {{target_logits, span_bytes(mul_sat({mt, vocab}), 4)}, {slot_tok, span_bytes(mt, 4)},
                        {offsets, span_bytes(nt + (tgt ? 1 : 0), 4)}, {k, span_bytes(nt, 4)},
-                       {draft_logits, span_bytes(nd * (drf ? draft_vocab : 0), 4)}};
+                       {draft_logits, span_bytes(mul_sat({nd, drf ? draft_vocab : 0}), 4)}};
     if (outputs_alias(out, in)) return DSV_ERR_INVALID_ARG;
   }
 

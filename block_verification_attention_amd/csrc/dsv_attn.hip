@@ -1574,11 +1574,13 @@ static dsv_status verify_attn_impl(const dsv_attn_args *a, const dsv::PackOut *p
     const int64_t pr = prefill ? a->pf_q_rows : 0, npf = prefill ? a->n_pf : 0;
     const int64_t hq = a->hq, hkv = a->hkv, d = a->d;
     const int64_t pool_elems =
-        a->pool_rows > 0 ? (hkv - 1) * a->stride_head + (a->pool_rows - 1) * a->stride_row + d : 0;
-    const Span out[] = {{a->out, span_bytes(m * hq * d, e)},
-                        {a->lse, span_bytes(m * hq, 4)},
-                        {a->pf_out, span_bytes(pr * hq * d, e)},
-                        {a->pf_lse, span_bytes(pr * hq, 4)},
+        a->pool_rows > 0 ? add_sat(add_sat(mul_sat({hkv - 1, a->stride_head}),
+                                           mul_sat({a->pool_rows - 1, a->stride_row})), d)
+                         : 0;
+    const Span out[] = {{a->out, span_bytes(mul_sat({m, hq, d}), e)},
+                        {a->lse, span_bytes(mul_sat({m, hq}), 4)},
+                        {a->pf_out, span_bytes(mul_sat({pr, hq, d}), e)},
+                        {a->pf_lse, span_bytes(mul_sat({pr, hq}), 4)},
                         {use_scratch ? nullptr : ws, pl.ws_o + pl.ws_lse},
                         {a->status, 4},
                         {po ? po->offsets : nullptr, span_bytes(n + 1, 4)},
@@ -1586,23 +1588,23 @@ static dsv_status verify_attn_impl(const dsv_attn_args *a, const dsv::PackOut *p
                         {po ? po->slot_tok : nullptr, span_bytes(m, 4)},
                         {po ? po->slot_pos : nullptr, span_bytes(m, 4)},
                         {po ? po->slot_cache_loc : nullptr, span_bytes(m, 8)}};
-    const Span in[] = {{a->q, span_bytes(m * hq * d, e)},
-                       {a->k_new, span_bytes(m * hkv * d, e)},
-                       {a->v_new, span_bytes(m * hkv * d, e)},
+    const Span in[] = {{a->q, span_bytes(mul_sat({m, hq, d}), e)},
+                       {a->k_new, span_bytes(mul_sat({m, hkv, d}), e)},
+                       {a->v_new, span_bytes(mul_sat({m, hkv, d}), e)},
                        {po ? nullptr : a->offsets, span_bytes(n + 1, 4)},
                        {a->k, span_bytes(n, 4)},
                        {a->ctx_len, span_bytes(n, 4)},
                        {a->kv_base, span_bytes(n, 8)},
                        {po ? nullptr : a->slot_cache_loc, span_bytes(m, 8)},
-                       {a->kv_index, span_bytes(n * a->kv_index_stride, 4)},
-                       {po ? po->block_tokens : nullptr, span_bytes(n * a->W, 4)},
+                       {a->kv_index, span_bytes(mul_sat({n, a->kv_index_stride}), 4)},
+                       {po ? po->block_tokens : nullptr, span_bytes(mul_sat({n, a->W}), 4)},
                        {a->pf_q_start, span_bytes(npf, 4)},
                        {a->pf_q_len, span_bytes(npf, 4)},
                        {a->pf_ctx_len, span_bytes(npf, 4)},
                        {a->pf_kv_base, span_bytes(npf, 8)},
-                       {a->pf_q, span_bytes(pr * hq * d, e)},
-                       {a->pf_k_new, span_bytes(pr * hkv * d, e)},
-                       {a->pf_v_new, span_bytes(pr * hkv * d, e)}};
+                       {a->pf_q, span_bytes(mul_sat({pr, hq, d}), e)},
+                       {a->pf_k_new, span_bytes(mul_sat({pr, hkv, d}), e)},
+                       {a->pf_v_new, span_bytes(mul_sat({pr, hkv, d}), e)}};
     const Span pools[] = {{a->k_pool, span_bytes(pool_elems, e)}, {a->v_pool, span_bytes(pool_elems, e)}};
     if (outputs_alias(out, in, pools)) return DSV_ERR_INVALID_ARG;
   }

@@ -175,8 +175,13 @@ inline int64_t mul_sat(std::initializer_list<int64_t> xs) {
 inline bool launch_fits(int64_t blocks, int64_t threads) {
   return blocks >= 0 && blocks <= INT32_MAX && blocks * threads <= (int64_t)UINT32_MAX;
 }
-// Bytes of n elements of elem bytes (none for n <= 0).
-inline size_t span_bytes(int64_t n, size_t elem) { return n > 0 ? (size_t)n * elem : 0; }
+// Sum of non-negative counts, saturating at INT64_MAX.
+inline int64_t add_sat(int64_t a, int64_t b) { return a > INT64_MAX - b ? INT64_MAX : a + b; }
+// Bytes of n elements of elem bytes (none for n <= 0; saturating at SIZE_MAX).
+inline size_t span_bytes(int64_t n, size_t elem) {
+  if (n <= 0) return 0;
+  return (uint64_t)n > SIZE_MAX / elem ? SIZE_MAX : (size_t)n * elem;
+}
 // True when an output shares a byte with another output or with an input, or a read-write
 // buffer (shared) with an output or an input.  Inputs may share bytes with each other, and
 // read-write buffers with each other (two views of one allocation, such as K and V pools
