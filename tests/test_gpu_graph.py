@@ -104,3 +104,61 @@ def test_next_rows_graph_capture_replays_match_eager():
                 ok = torch.equal(t, e)
             assert ok, f"replay {r}, output {j}"
     assert int(st.item()) == 0
+
+
+def test_mixed_and_noalloc_graph_capture_replays_match_eager():
+    """The mixed call (a prefill set beside the verification set in one dsv_verify_attn) and
+    the no-allocation entry point (split partials in the library's scratch array, the call
+    meant for code under capture), captured in one graph: three replays, with eager work and
+    synchronisation between them, reproduce the eager outputs bit for bit."""
+    st = dsv.new_status(DEV)
+    c = wl.make_mixed_case(95, hq=8, hkv=2, d=128, k=[3, 16], ctx_len=[40, 1300], m_bs=20,
+                           pf_q_len=[300, 77], pf_ctx=[0, 33])
+    d = device_case(c)
+    packed = gpu_pack(c, d)
+    pf = c["prefill"]
+    pf_q = to_dev(pf["q"])
+    prefill = dsv.Prefill(q_start=to_dev(pf["q_start"]), q_len=to_dev(pf["q_len"]),
+                          ctx_len=to_dev(pf["ctx_len"]), kv_base=to_dev(pf["kv_base"]), q=pf_q,
+                          out=torch.zeros_like(pf_q), max_len=pf["max_len"],
+                          lse=torch.zeros((pf_q.shape[0], c["hq"]), device=DEV))
+    out = torch.zeros_like(d["q"])
+    lse = torch.zeros((c["m_bs"], c["hq"]), device=DEV)
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device=DEV)
+    c2 = small_case(96, hq=12, hkv=4, d=128, k=(16, 9, 1, 12), ctx=(2000, 700, 5, 1300))
+    d2 = device_case(c2)
+    packed2 = gpu_pack(c2, d2)
+    out2 = torch.zeros_like(d2["q"])
+    lse2 = torch.zeros((c2["m_bs"], c2["hq"]), device=DEV)
+
+    def calls():
+        a = dsv.attn_args(d["q"], d["k_pool"], d["v_pool"], packed["offsets"], d["k"], d["ctx_len"],
+                          d["kv_base"], W=16, max_ctx=1300, out=out, status=st, lse=lse,
+                          k_new=d["k_new"], v_new=d["v_new"], slot_cache_loc=packed["slot_cache_loc"],
+                          kv_chunk=256, workspace=ws, prefill=prefill)
+        dsv.verify_attn_call(a)
+        a2 = dsv.attn_args(d2["q"], d2["k_pool"], d2["v_pool"], packed2["offsets"], d2["k"],
+                           d2["ctx_len"], d2["kv_base"], W=16, max_ctx=2000, out=out2, status=st,
+                           lse=lse2, k_new=d2["k_new"], v_new=d2["v_new"],
+                           slot_cache_loc=packed2["slot_cache_loc"], kv_chunk=256)
+        dsv.verify_attn_noalloc_call(a2)
+
+    calls()
+    torch.cuda.synchronize()
+    results = lambda: [out, lse, prefill.out, prefill.lse, out2, lse2]  # noqa: E731
+    eager = [t.clone() for t in results()]
+    # outputs finite (tail rows zero-filled); lse of the tail rows is -inf by definition
+    assert all(bool(torch.isfinite(eager[j].float()).all()) for j in (0, 2, 3, 4))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    for r in range(3):
+        for t in results():
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for j, (t, e) in enumerate(zip(results(), eager)):
+            bits = torch.int16 if t.dtype == torch.bfloat16 else torch.int32
+            assert torch.equal(t.view(bits), e.view(bits)), f"replay {r}, output {j}"
+    assert int(st.item()) == 0
