@@ -42,7 +42,7 @@ PROFILED_KERNEL = "attn_bf16_kernel<128, 8, false, 64, 2, false>"
 # WRITE_SIZE runs (profiles/attn_verify_cfg3_hbm_traffic.md, calibrated there against the
 # streaming-read probe and a pool copy), valid for the kernel source with this SHA-256 only.
 COUNTED_SOURCE = ("block_verification_attention_amd/csrc/dsv_attn.hip",
-                  "ea5b2e328d4b04abc4cab65542afe85410dc471e4e514f29e8aa26f3cbfcba40")
+                  "5fd0cb7465a7f6dab4c7ca3dd90329fb429e0a4559903db1d132d0ab8e6325c8")
 COUNTED_READ_BYTES = 270_444_171
 COUNTED_WRITE_BYTES = 5_523_292
 
@@ -260,19 +260,19 @@ def time_features(dev, copies: int = 2, iters: int = 10):
     return res
 
 
-def time_prefill(dev, iters: int = 20, lens=(4096,) * 4, hq: int = 32, hkv: int = 8, seed: int = 5005):
+def time_prefill(dev, iters: int = 20, lens=(4096,) * 4, hq: int = 32, hkv: int = 8, seed: int = 5005,
+                 d: int = 128):
     """Prefill attention with the 128-row wide tile (bf16 MFMA-bound).  Default: the
     mixed workload's prefill set, 4 fresh requests of 4096 causal rows (context 0), 32 query /
     8 KV heads, head_dim 128, seeded N(0,1) * 0.5 inputs made on the device.  Work per call:
     sum over rows of the visible keys x query heads x 128 x 4 flop (Q.K and P.V): 5.50e11 flop
     for the default set.  Device time per call from HIP events around each dsv_verify_attn call
     (prefill only, the pool already holding the rows' K/V), median of `iters`, against the
-    dense bf16 MFMA peak of 2.5 PFLOP/s.  `lens`, `hq` and `hkv` give other sets (ragged
-    lengths, fewer KV heads)."""
+    dense bf16 MFMA peak of 2.5 PFLOP/s.  `lens`, `hq`, `hkv` and `d` give other sets (ragged
+    lengths, fewer KV heads, head_dim 256)."""
     import numpy as np
     import torch
     import block_verification_attention_amd as dsv
-    d = 128
     lens = [int(x) for x in lens]
     n_req = len(lens)
     g = torch.Generator(device=dev)
@@ -305,8 +305,9 @@ def time_prefill(dev, iters: int = 20, lens=(4096,) * 4, hq: int = 32, hkv: int 
     tflops = flop / (us * 1e-6) / 1e12
     shape = (f"{n_req} x {lens[0]}" if len(set(lens)) == 1
              else "lengths " + ", ".join(str(n) for n in lens))
-    return {"workload": f"prefill, {shape} causal rows, {hq}/{hkv} heads, head_dim 128, bf16",
-            "kernel": "attn_bf16_kernel<128, 8, true, 32, 1, false>", "us": us, "flop": flop,
+    return {"workload": f"prefill, {shape} causal rows, {hq}/{hkv} heads, head_dim {d}, bf16",
+            "kernel": f"attn_bf16_kernel<{d}, 8, true, {64 if d == 64 else 32}, 1, false>", "us": us,
+            "flop": flop,
             "TFLOPs": tflops, "peak_TFLOPs": 2500.0, "frac": tflops / 2500.0,
             "status": int(st.item())}
 
@@ -857,6 +858,8 @@ def main():
     # ragged lengths with 2 KV heads (8 query heads each): the row blocks of a request are
     # spread over the XCDs by the launch's block order
     res["prefill_ragged"] = time_prefill(dev, lens=(4096, 1024, 1024, 1024), hq=16, hkv=2, seed=5006)
+    # head_dim 256 (16 query / 8 KV heads)
+    res["prefill_d256"] = time_prefill(dev, hq=16, hkv=8, seed=5007, d=256)
     res["other_verify"] = time_other_verify(dev, ev)
     res["mixed_launch"] = time_mixed(dev)
     if args.cpu_sample > 0:

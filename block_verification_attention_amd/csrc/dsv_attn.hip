@@ -49,12 +49,13 @@ constexpr int kXcds = 8;     // dispatch places block b on XCD b % 8
 // Waves with at most this many 16-byte loads per tile stage two tiles in registers (more
 // would push the hot shapes past the register budget of two waves per SIMD).
 constexpr int kTwoSetMaxLoads = 4;
-// Prefill: waves per workgroup and 16-row query tiles per wave (two 128-row tiles at head_dim
-// 128, one at 64; 64 rows at head_dim 256, whose wave needs the whole register file for its
-// 16 x 256 output and query fragments).  At head_dim 128 a wave holds two query tiles, so that
-// every K and V operand it reads from LDS feeds two MFMAs.
+// Prefill: 8 waves per workgroup at every head_dim, two per SIMD, and 16-row query tiles per
+// wave (two 128-row tiles at head_dim 128, one 128-row tile at 64 and 256).  At head_dim 128
+// a wave holds two query tiles, so that every K and V operand it reads from LDS feeds two
+// MFMAs; at head_dim 256 one tile's 16 x 256 output and query fragments fill most of a wave's
+// share of the register file.
 constexpr int pf_qtiles(int D) { return D == 128 ? 2 : 1; }
-constexpr int pf_waves(int D) { return D >= 256 ? 4 : 8; }
+constexpr int pf_waves(int) { return 8; }
 constexpr int pf_rows(int D) { return pf_waves(D) * 16 * pf_qtiles(D); }
 // Prefill KV tile rows at head_dim 128 (the two query tiles double the score registers).
 constexpr int kPfTile128 = 32;
@@ -216,11 +217,11 @@ constexpr float kRescaleSlack = 8.0f;
 // ---------------------------------------------------------------------------
 template <int D, int NW, bool PF>
 constexpr int waves_per_eu_hint() {
-  // small workgroups and the 4-wave head_dim-256 prefill get the whole register file; 3..8
-  // waves are asked to fit 2 waves/SIMD, and at head_dim 128 and 256 exactly 2 (a third wave
-  // per SIMD cannot host another workgroup of this size, and tighter register budgets cost
-  // the tile loop its loads in flight); head_dim-64 kernels may run more per SIMD
-  return (NW <= 2 || (D == 256 && NW <= 4 && PF)) ? 1 : (NW <= 8 ? 2 : 1);
+  // small workgroups get the whole register file; 3..8 waves are asked to fit 2 waves/SIMD,
+  // and at head_dim 128 and 256 exactly 2 (a third wave per SIMD cannot host another
+  // workgroup of this size, and tighter register budgets cost the tile loop its loads in
+  // flight); head_dim-64 kernels may run more per SIMD
+  return NW <= 2 ? 1 : (NW <= 8 ? 2 : 1);
 }
 
 template <int D, int NW, bool PF, int TILE, int HV, bool MAP>
@@ -673,12 +674,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
       }
       return a;
     };
-    // prefill (one 32-row step per tile): the tile's V operands are read first, so
-    // that their LDS latency runs behind the row maximum, the next tile's Q.K and the
-    // exponentials
-    constexpr int VPRE = PF ? KK * DB : 1;
+    // prefill (one 32-row step per tile) up to head_dim 128: the tile's V operands are read
+    // first, so that their LDS latency runs behind the row maximum, the next tile's Q.K and
+    // the exponentials.  At head_dim 256 they would take 64 more registers than two waves per
+    // SIMD leave, so they are read where used.
+    constexpr bool VREAD = PF && D <= 128;
+    constexpr int VPRE = VREAD ? KK * DB : 1;
     bf16x8 va[VPRE];
-    if constexpr (PF) {
+    if constexpr (VREAD) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
@@ -743,7 +746,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(waves_p
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         bf16x8 a;
-        if constexpr (PF)
+        if constexpr (VREAD)
           a = va[kk * DB + db];
         else
           a = v_operand(kk, db);
