@@ -42,7 +42,7 @@ PROFILED_KERNEL = "attn_bf16_kernel<128, 8, false, 64, 2, false>"
 # WRITE_SIZE runs (profiles/attn_verify_cfg3_hbm_traffic.md, calibrated there against the
 # streaming-read probe and a pool copy), valid for the kernel source with this SHA-256 only.
 COUNTED_SOURCE = ("block_verification_attention_amd/csrc/dsv_attn.hip",
-                  "5fd0cb7465a7f6dab4c7ca3dd90329fb429e0a4559903db1d132d0ab8e6325c8")
+                  "93614c957bcc3d73417ec190649708498c47672ea95e025a866a7f33a8bd6ecf")
 COUNTED_READ_BYTES = 270_444_171
 COUNTED_WRITE_BYTES = 5_523_292
 
@@ -860,6 +860,8 @@ def main():
     res["prefill_ragged"] = time_prefill(dev, lens=(4096, 1024, 1024, 1024), hq=16, hkv=2, seed=5006)
     # head_dim 256 (16 query / 8 KV heads)
     res["prefill_d256"] = time_prefill(dev, hq=16, hkv=8, seed=5007, d=256)
+    # head_dim 64 (32 query / 8 KV heads)
+    res["prefill_d64"] = time_prefill(dev, hq=32, hkv=8, seed=5008, d=64)
     res["other_verify"] = time_other_verify(dev, ev)
     res["mixed_launch"] = time_mixed(dev)
     if args.cpu_sample > 0:

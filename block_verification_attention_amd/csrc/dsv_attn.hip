@@ -50,11 +50,11 @@ constexpr int kXcds = 8;     // dispatch places block b on XCD b % 8
 // would push the hot shapes past the register budget of two waves per SIMD).
 constexpr int kTwoSetMaxLoads = 4;
 // Prefill: 8 waves per workgroup at every head_dim, two per SIMD, and 16-row query tiles per
-// wave (two 128-row tiles at head_dim 128, one 128-row tile at 64 and 256).  At head_dim 128
-// a wave holds two query tiles, so that every K and V operand it reads from LDS feeds two
-// MFMAs; at head_dim 256 one tile's 16 x 256 output and query fragments fill most of a wave's
-// share of the register file.
-constexpr int pf_qtiles(int D) { return D == 128 ? 2 : 1; }
+// wave (two at head_dim 64 and 128: two 128-row tiles per workgroup; one at 256: one 128-row
+// tile).  With two query tiles a wave's every K and V operand read from LDS feeds two MFMAs;
+// at head_dim 256 one tile's 16 x 256 output and query fragments fill most of a wave's share
+// of the register file.
+constexpr int pf_qtiles(int D) { return D <= 128 ? 2 : 1; }
 constexpr int pf_waves(int) { return 8; }
 constexpr int pf_rows(int D) { return pf_waves(D) * 16 * pf_qtiles(D); }
 // Prefill KV tile rows at head_dim 128 (the two query tiles double the score registers).

@@ -104,11 +104,11 @@ def test_prefill_rotation_wraps(d_head, hq, hkv, q_len, ctx):
 # Query lengths and contexts around each head_dim's tile edges, so that rows end inside a
 # wave, a wave's tile or a workgroup's row block, and contexts start the diagonal mid-tile:
 # head_dim 128 runs 256-row workgroups of 8 waves x 32 rows on 32-row KV tiles; head_dim 64
-# 128-row workgroups of 8 waves x 16 rows on 64-row KV tiles; head_dim 256 128-row workgroups
+# 256-row workgroups of 8 waves x 32 rows on 64-row KV tiles; head_dim 256 128-row workgroups
 # of 8 waves x 16 rows on 32-row KV tiles.
 _EDGES = {
     128: ([1, 15, 16, 17, 31, 32, 33, 255, 256, 257, 511, 513], [0, 5, 31, 32, 33, 64, 100, 0, 7, 130, 1, 3], 8, 2),
-    64: ([1, 15, 16, 17, 63, 64, 65, 127, 128, 129, 255, 257], [0, 5, 63, 64, 65, 128, 100, 0, 7, 130, 1, 3], 4, 1),
+    64: ([1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 255, 257], [0, 5, 63, 64, 65, 128, 100, 0, 7, 130, 1, 3], 4, 1),
     256: ([1, 15, 16, 17, 31, 32, 33, 127, 128, 129, 255, 257], [0, 5, 31, 32, 33, 64, 100, 0, 7, 130, 1, 3], 6, 2),
 }
 
