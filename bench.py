@@ -42,7 +42,7 @@ PROFILED_KERNEL = "attn_bf16_kernel<128, 8, false, 64, 2, false>"
 # WRITE_SIZE runs (profiles/attn_verify_cfg3_hbm_traffic.md, calibrated there against the
 # streaming-read probe and a pool copy), valid for the kernel source with this SHA-256 only.
 COUNTED_SOURCE = ("block_verification_attention_amd/csrc/dsv_attn.hip",
-                  "93614c957bcc3d73417ec190649708498c47672ea95e025a866a7f33a8bd6ecf")
+                  "6e699b35b09c78c1dcc6aa99e0ac27d28835634dd83b1c9817683377deda981a")
 COUNTED_READ_BYTES = 270_444_171
 COUNTED_WRITE_BYTES = 5_523_292
 
@@ -384,7 +384,8 @@ def time_other_verify(dev, ev, iters: int = 20):
     32 requests sharing 256 slots at contexts U[4096, 8192], 24 query / 2 KV heads, head_dim
     256 (12 query heads per KV head); and 60 requests sharing 480 slots at contexts
     U[8192, 32768], 32 / 8 heads, head_dim 128.  Also the first shape's requests with 8 query
-    heads on 8 KV heads (one per KV head, head_dim 256).  Kernel time from the start/stop events
+    heads on 8 KV heads (one per KV head, head_dim 256) and with 64 query heads on 8 KV heads
+    (eight per KV head, head_dim 128).  Kernel time from the start/stop events
     attached to the verification kernel's launch (median of `iters`), algorithmic KV bytes
     (every visible K and V row once) over it, against 8 TB/s."""
     import numpy as np
@@ -396,6 +397,7 @@ def time_other_verify(dev, ev, iters: int = 20):
         "32x256_slots_ctx4k-8k_24q2kv_d256": (4, 32, 256, 4096, 8193, 24, 2, 256, 2),
         "60x480_slots_ctx8k-32k_32q8kv_d128": (5, 60, 480, 8192, 32769, 32, 8, 128, 1),
         "32x256_slots_ctx4k-8k_8q8kv_d256": (4, 32, 256, 4096, 8193, 8, 8, 256, 1),
+        "32x256_slots_ctx4k-8k_64q8kv_d128": (4, 32, 256, 4096, 8193, 64, 8, 128, 1),
     }
     for name, (cfg, n, m_bs, lo, hi, hq, hkv, d, copies) in shapes.items():
         g = wl.rng(cfg, 0)

@@ -1287,10 +1287,11 @@ static int verify_heads_per_wg(int D, int G) {
   const int cap = D >= 256 ? kWideHeadsPerWg : (D >= 128 ? 8 : G);
   const int groups = (G + cap - 1) / cap;
   int gw = (G + groups - 1) / groups;
-  // head_dim 128: workgroups of 2, 3 or 6 one-head waves spill (the tile's wave loads do not
-  // split evenly over them); such groups run padded to 4 or 8 heads
+  // head_dim 128: workgroups of 2, 3 or 6 one-head waves spill and of 5 or 7 stream slowly
+  // (the tile's 32 wave loads do not split evenly over them: one staged tile in registers
+  // instead of two); such groups run padded to 4 or 8 heads
   if (D == 128 && (gw == 2 || gw == 3)) gw = 4;
-  if (D == 128 && gw == 6) gw = 8;
+  if (D == 128 && gw >= 5 && gw <= 7) gw = 8;
   return gw;
 }
 static int verify_head_groups(int D, int G) {
@@ -1416,13 +1417,11 @@ static int launch_verify_g(const AttnParams &p, int grid, hipStream_t s, hipEven
       default: return -1;
     }
   } else if constexpr (D == 128) {
-    // groups padded to 1 or 4 heads (two KV halves) or 5, 7, 8 heads (one half): the shapes
-    // that fit two waves per SIMD without spilling
+    // groups padded to 1 or 4 heads (two KV halves) or 8 heads (one half): the shapes that
+    // fit two waves per SIMD without spilling and split a tile's loads evenly
     switch (p.GW) {
       case 1: return launch_attn<D, 2, false, 2>(p, grid, s, e0, e1);
       case 4: return launch_attn<D, 8, false, 2>(p, grid, s, e0, e1);
-      case 5: return launch_attn<D, 5, false>(p, grid, s, e0, e1);
-      case 7: return launch_attn<D, 7, false>(p, grid, s, e0, e1);
       case 8: return launch_attn<D, 8, false>(p, grid, s, e0, e1);
       default: return -1;
     }
