@@ -1331,14 +1331,18 @@ static Plan make_plan(const dsv_attn_args *a) {
     const int G = a->hkv > 0 ? a->hq / a->hkv : 1;
     const int GW = verify_heads_per_wg(a->d, G);
     const int64_t units = (int64_t)a->n_bs * a->hkv * verify_head_groups(a->d, G);
-    // wave groups in flight: two per SIMD (512 groups of G waves, or 256 two-half ones); the
-    // wide-head workgroups (4 waves, two per CU at a time) aim at three rounds: the head
-    // groups that per-request regrouping drops at run time (a request needs ceil(G k_i / 64)) leave
-    // fewer workgroups than counted here, and a plan for two rounds left 1.3 of them on the
-    // 32-request head_dim-256 set, its sparse second round idling most CUs (197 us against
-    // 165 us for 1.7 rounds)
+    // wave groups in flight: two per SIMD (512 groups of G waves, or 256 two-half ones).
+    // Per-request regrouping drops at run time the head groups a request does not need (it
+    // needs ceil(G k_i / 16) waves), leaving fewer workgroups than counted here, so plans with
+    // head groups aim at more rounds: the wide-head workgroups (head_dim 256: 4 waves, two per
+    // CU) at three -- a plan for two rounds left 1.3 of them on the 32-request head_dim-256
+    // set, its sparse second round idling most CUs (197 us against 165 us for 1.7 rounds) --
+    // and head_dim 128's 8-wave ones (one per CU) at four (9 heads per KV head 324 -> 290 us,
+    // 16 heads 328 -> 314 us on 32 requests at contexts 4k-8k)
     const int64_t cus = device_cus();
-    const int64_t wgs = a->d >= 256 ? 6 * cus : 2 * cus / verify_halves(GW);
+    const int64_t wgs = a->d >= 256                       ? 6 * cus
+                        : verify_head_groups(a->d, G) > 1 ? 4 * cus
+                                                          : 2 * cus / verify_halves(GW);
     int64_t target = (wgs + units - 1) / units;
     if (target < 1) target = 1;
     if (target > 64) target = 64;
