@@ -1337,12 +1337,14 @@ static Plan make_plan(const dsv_attn_args *a) {
     // head groups aim at more rounds: the wide-head workgroups (head_dim 256: 4 waves, two per
     // CU) at three -- a plan for two rounds left 1.3 of them on the 32-request head_dim-256
     // set, its sparse second round idling most CUs (197 us against 165 us for 1.7 rounds) --
-    // and head_dim 128's 8-wave ones (one per CU) at four (9 heads per KV head 324 -> 290 us,
-    // 16 heads 328 -> 314 us on 32 requests at contexts 4k-8k)
+    // and head_dim 128's 8-wave ones (one per CU) at twice the workgroups (9 heads per KV head
+    // 324 -> 290 us, 16 heads 328 -> 314 us on 32 requests at contexts 4k-8k).  So do sets
+    // with fewer KV heads than XCDs, whose units place a request's splits on few XCDs (on
+    // the same 32 requests: head_dim 64 with 16/4 heads 69 -> 54 us, 4/4 90 -> 51 us; head_dim
+    // 128 with 16/4 heads 116 -> 93 us, 4/4 137 -> 108 us; 8 KV heads keep their plan).
     const int64_t cus = device_cus();
-    const int64_t wgs = a->d >= 256                       ? 6 * cus
-                        : verify_head_groups(a->d, G) > 1 ? 4 * cus
-                                                          : 2 * cus / verify_halves(GW);
+    const bool more = verify_head_groups(a->d, G) > 1 || a->hkv < kXcds;
+    const int64_t wgs = a->d >= 256 ? 6 * cus : (more ? 4 : 2) * cus / verify_halves(GW);
     int64_t target = (wgs + units - 1) / units;
     if (target < 1) target = 1;
     if (target > 64) target = 64;
