@@ -1289,9 +1289,12 @@ static int verify_heads_per_wg(int D, int G) {
   int gw = (G + groups - 1) / groups;
   // head_dim 128: workgroups of 2, 3 or 6 one-head waves spill and of 5 or 7 stream slowly
   // (the tile's 32 wave loads do not split evenly over them: one staged tile in registers
-  // instead of two); such groups run padded to 4 or 8 heads
+  // instead of two); such groups run padded to 4 or 8 heads.  At head_dim 64 groups of 5 to
+  // 7 (16 wave loads per tile) run padded to 8 as well (5 heads per KV head 130 -> 121 us,
+  // 7 heads 150 -> 126 us on 32 requests at contexts 4k-8k); larger groups keep one wave per
+  // head (padding 9 to 15 heads to 16 waves was slower at 12)
   if (D == 128 && (gw == 2 || gw == 3)) gw = 4;
-  if (D == 128 && gw >= 5 && gw <= 7) gw = 8;
+  if (D <= 128 && gw >= 5 && gw <= 7) gw = 8;
   return gw;
 }
 static int verify_head_groups(int D, int G) {
@@ -1433,15 +1436,12 @@ static int launch_verify_g(const AttnParams &p, int grid, hipStream_t s, hipEven
     }
   } else {
     // head_dim 64: every group of up to 16 heads in one workgroup; up to 4 heads in two KV
-    // halves (verify_halves)
+    // halves (verify_halves); groups of 5 to 7 padded to 8
     switch (p.GW) {
       case 1: return launch_attn<D, 2, false, 2>(p, grid, s, e0, e1);
       case 2: return launch_attn<D, 4, false, 2>(p, grid, s, e0, e1);
       case 3: return launch_attn<D, 6, false, 2>(p, grid, s, e0, e1);
       case 4: return launch_attn<D, 8, false, 2>(p, grid, s, e0, e1);
-      case 5: return launch_attn<D, 5, false>(p, grid, s, e0, e1);
-      case 6: return launch_attn<D, 6, false>(p, grid, s, e0, e1);
-      case 7: return launch_attn<D, 7, false>(p, grid, s, e0, e1);
       case 8: return launch_attn<D, 8, false>(p, grid, s, e0, e1);
       case 9: return launch_attn<D, 9, false>(p, grid, s, e0, e1);
       case 10: return launch_attn<D, 10, false>(p, grid, s, e0, e1);

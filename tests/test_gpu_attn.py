@@ -39,8 +39,9 @@ def test_config1_fp32():
                                             # head_dim 256 with one or two query heads per KV
                                             # head (waves without heads in the 4-wave kernel)
                                             (256, 2, 1), (256, 8, 4),
-                                            # head_dim 128 groups of 5 and 7 (padded to 8 waves)
-                                            (128, 5, 1), (128, 14, 2)])
+                                            # head_dim 128 groups of 5 and 7, head_dim 64 of
+                                            # 7 and 6 (padded to 8 waves)
+                                            (128, 5, 1), (128, 14, 2), (64, 7, 1), (64, 12, 2)])
 @pytest.mark.parametrize("kv_chunk", [0, 64, 256])
 def test_bf16_ragged(d_head, hq, hkv, kv_chunk):
     c = small_case(10 + d_head + hq, hq=hq, hkv=hkv, d=d_head,
