@@ -42,7 +42,7 @@ PROFILED_KERNEL = "attn_bf16_kernel<128, 8, false, 64, 2, false>"
 # WRITE_SIZE runs (profiles/attn_verify_cfg3_hbm_traffic.md, calibrated there against the
 # streaming-read probe and a pool copy), valid for the kernel source with this SHA-256 only.
 COUNTED_SOURCE = ("block_verification_attention_amd/csrc/dsv_attn.hip",
-                  "2a3928781fc20113f02953d6cfc3ab15598b18bc218d827e1cb89a4a53619ee1")
+                  "e33a614536fe03d2c045884511b6ee94b89c5054c76af562c1448b7104bf82f8")
 COUNTED_READ_BYTES = 270_444_171
 COUNTED_WRITE_BYTES = 5_523_292
 

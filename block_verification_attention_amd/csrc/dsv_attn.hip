@@ -1345,9 +1345,14 @@ static Plan make_plan(const dsv_attn_args *a) {
     // with fewer KV heads than XCDs, whose units place a request's splits on few XCDs (on
     // the same 32 requests: head_dim 64 with 16/4 heads 69 -> 54 us, 4/4 90 -> 51 us; head_dim
     // 128 with 16/4 heads 116 -> 93 us, 4/4 137 -> 108 us; 8 KV heads keep their plan).
+    // At head_dim 256 a KV head served by one workgroup (up to 4 query heads) with 8 or more
+    // KV heads takes ten per CU: its workgroups hold one or two computing waves and many
+    // units, and shorter splits balance the XCDs better (32 requests at contexts 4k-8k, 8 KV
+    // heads: one query head per KV head 309 -> 284 us, two 317 -> 295 us, four 332 -> 321 us;
+    // with 2 KV heads the splits get too short: four heads 93 -> 98 us, kept at six).
     const int64_t cus = device_cus();
     const bool more = verify_head_groups(a->d, G) > 1 || a->hkv < kXcds;
-    const int64_t wgs = a->d >= 256 ? 6 * cus : (more ? 4 : 2) * cus / verify_halves(GW);
+    const int64_t wgs = a->d >= 256 ? (more ? 6 : 10) * cus : (more ? 4 : 2) * cus / verify_halves(GW);
     int64_t target = (wgs + units - 1) / units;
     if (target < 1) target = 1;
     if (target > 64) target = 64;

@@ -41,7 +41,10 @@ def test_config1_fp32():
                                             (256, 2, 1), (256, 8, 4),
                                             # head_dim 128 groups of 5 and 7, head_dim 64 of
                                             # 7 and 6 (padded to 8 waves)
-                                            (128, 5, 1), (128, 14, 2), (64, 7, 1), (64, 12, 2)])
+                                            (128, 5, 1), (128, 14, 2), (64, 7, 1), (64, 12, 2),
+                                            # head_dim 256 with 8 KV heads and one workgroup
+                                            # per KV head (the ten-per-CU split plan)
+                                            (256, 8, 8), (256, 32, 8)])
 @pytest.mark.parametrize("kv_chunk", [0, 64, 256])
 def test_bf16_ragged(d_head, hq, hkv, kv_chunk):
     c = small_case(10 + d_head + hq, hq=hq, hkv=hkv, d=d_head,

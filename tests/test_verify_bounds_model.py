@@ -68,8 +68,9 @@ def plan(n_bs, hkv, G, max_ctx, W, kv_chunk, cus=256):
     rows = max_ctx + W
     chunk = kv_chunk
     if chunk <= 0:
-        units = n_bs * hkv * ((G + heads_per_wg(G) - 1) // heads_per_wg(G))
-        wgs = 6 * cus
+        hg = (G + heads_per_wg(G) - 1) // heads_per_wg(G)
+        units = n_bs * hkv * hg
+        wgs = (6 if hg > 1 or hkv < XCDS else 10) * cus
         target = min(max((wgs + units - 1) // units, 1), 64)
         chunk = max(rows // target // K_TILE_KV * K_TILE_KV, K_TILE_KV)
         if units >= wgs and chunk > 4096:
@@ -262,7 +263,8 @@ def _case(hq, hkv, k, ctx, W=16, extra_tail=4):
 RAGGED = ((16, 5, 0, 11, 1, 16, 3), (700, 0, 40, 63, 64, 1000, 129))
 
 
-@pytest.mark.parametrize("hq,hkv", [(4, 4), (2, 1), (8, 4), (3, 1), (6, 2), (4, 1), (24, 2), (12, 1)])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (2, 1), (8, 4), (3, 1), (6, 2), (4, 1), (24, 2), (12, 1),
+                                     (8, 8), (32, 8)])
 @pytest.mark.parametrize("kv_chunk", [0, 64, 256])
 def test_head_dim_256_addresses_in_bounds(hq, hkv, kv_chunk):
     b = Bounds()
